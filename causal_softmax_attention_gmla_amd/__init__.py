@@ -1,0 +1,268 @@
+"""Causal softmax attention for Gated MLA layers on one MI355X (gfx950).
+
+Thin binding over libgmla.so (C ABI in include/gmla.h).  These functions check
+that tensor shapes agree with the sizes they pass, allocate outputs with PyTorch
+(device memory only), and hand raw device pointers plus the current HIP stream to
+the library; every arithmetic step runs in the library's HIP kernels.
+
+    attend_prefill(q, k, v, gate=None, scale=None, causal=True)   -> [B, T, H*D]
+    attend_decode(q, k, v, gate=None, scale=None, num_splits=0)   -> [B, H*D]
+    latent_expand(c, w_k, w_v)                                    -> (K, V)
+    gate_out(o_tilde, w_o=None, gate=None)                        -> Y
+    linear(x, w)                                                  -> x w^T
+    gated_mla(hidden_states, ..., num_heads, causal=True)         -> {"output", "latent_cache"}
+
+Formulas: "Gated MLA" (ai-engineer-exhaustive.pages.dev, research/kimik3/k3-gated-mla),
+sections "Start from familiar attention", "Split attention into heads", "The
+channel-wise output gate", "Requirements"; "Kimi K3 - Softmax over keys" and "Kimi K2 -
+Construct causal mask" (atlas.klimoza.dev).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import GMLA_BF16, GMLA_F32, GmlaError, LIB_PATH  # noqa: F401
+
+__all__ = ["attend_prefill", "attend_decode", "latent_expand", "gate_out", "linear", "gated_mla",
+           "decode_num_splits", "decode_workspace_bytes", "library", "GmlaError"]
+
+_DTYPES = {torch.float32: GMLA_F32, torch.bfloat16: GMLA_BF16}
+
+
+def library():
+    """The loaded ctypes handle of libgmla.so (raises if it is not built)."""
+    return _lib.load()
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16 only") from None
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+    return dev
+
+
+def _same_dtype(*ts):
+    d = None
+    for t in ts:
+        if t is None:
+            continue
+        if d is None:
+            d = t.dtype
+        elif t.dtype != d:
+            raise TypeError("all tensors must share one dtype")
+    return d
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attend_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor | None = None,
+                   *, scale: float | None = None, causal: bool = True, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Attention of every query against keys 0..t (causal) or all keys.
+
+    q, k, v: [B, T, H, D] with identical strides and a contiguous last axis (views
+    into [B, T, H*D] projections are fine).  gate: optional [B, T, H*D] logits; the
+    output is multiplied by sigmoid(gate) channel-wise.  Returns [B, T, H*D].
+    """
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, T, H, D]")
+    if k.stride() != q.stride() or v.stride() != q.stride() or q.stride(3) != 1:
+        raise ValueError("q, k, v need identical strides and a contiguous last axis")
+    if not isinstance(causal, bool):
+        raise TypeError("causal must be a bool")
+    B, T, H, D = q.shape
+    dev = _dev(q, k, v, gate, out)
+    _same_dtype(q, k, v, gate, out)
+    if gate is not None and (gate.shape != (B, T, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [B, T, H*D] tensor")
+    if out is None:
+        out = torch.empty((B, T, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (B, T, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, T, H*D] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    strides = (ctypes.c_int64 * 3)(q.stride(0), q.stride(1), q.stride(2))
+    st = _lib.load().gmla_attend_prefill(_dtype(q), B, T, H, D, float(scale), int(causal),
+                                         _ptr(q), _ptr(k), _ptr(v), strides, _ptr(gate), _ptr(out),
+                                         _stream(dev, stream))
+    _lib.check(st, "gmla_attend_prefill")
+    return out
+
+
+def decode_num_splits(B: int, H: int, N: int, D: int) -> int:
+    return _lib.load().gmla_decode_num_splits(B, H, N, D)
+
+
+def decode_workspace_bytes(B: int, H: int, N: int, D: int, num_splits: int = 0) -> int:
+    return _lib.load().gmla_decode_workspace_bytes(B, H, N, D, num_splits)
+
+
+def attend_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor | None = None,
+                  *, scale: float | None = None, num_splits: int = 0,
+                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """One query per (batch, head) at position N-1 against N cached keys.
+
+    q: [B, H, D] contiguous; k, v: [B, H, N, D] with identical strides and a
+    contiguous last axis; gate: optional [B, H*D].  Returns [B, H*D].
+    """
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, D] and k, v [B, H, N, D]")
+    B, H, N, D = k.shape
+    if q.shape != (B, H, D) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, D] tensor")
+    if k.stride() != v.stride() or k.stride(3) != 1:
+        raise ValueError("k, v need identical strides and a contiguous last axis")
+    dev = _dev(q, k, v, gate, out, workspace)
+    _same_dtype(q, k, v, gate, out)
+    if gate is not None and (gate.shape != (B, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [B, H*D] tensor")
+    if out is None:
+        out = torch.empty((B, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H*D] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    need = lib.gmla_decode_workspace_bytes(B, H, N, D, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    strides = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    st = lib.gmla_attend_decode(_dtype(q), B, H, N, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                strides, _ptr(gate), _ptr(out), _ptr(workspace), ws_bytes,
+                                int(num_splits), _stream(dev, stream))
+    _lib.check(st, "gmla_attend_decode")
+    return out
+
+
+def latent_expand(c: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, *, stream=None):
+    """K = C W_k^T and V = C W_v^T in one pass over C [..., d_c]; W_k, W_v [d_model, d_c]."""
+    d_c = c.shape[-1]
+    d_model = w_k.shape[0]
+    if w_k.shape != (d_model, d_c) or w_v.shape != (d_model, d_c):
+        raise ValueError("w_k and w_v must be [d_model, d_c]")
+    for t in (c, w_k, w_v):
+        if not t.is_contiguous():
+            raise ValueError("latent_expand takes contiguous tensors")
+    dev = _dev(c, w_k, w_v)
+    _same_dtype(c, w_k, w_v)
+    M = c.numel() // d_c
+    K = torch.empty((*c.shape[:-1], d_model), dtype=c.dtype, device=dev)
+    V = torch.empty_like(K)
+    st = _lib.load().gmla_latent_expand(_dtype(c), M, d_c, d_model, _ptr(c), _ptr(w_k), _ptr(w_v),
+                                        _ptr(K), _ptr(V), _stream(dev, stream))
+    _lib.check(st, "gmla_latent_expand")
+    return K, V
+
+
+def gate_out(o_tilde: torch.Tensor, w_o: torch.Tensor | None = None, gate: torch.Tensor | None = None,
+             *, stream=None) -> torch.Tensor:
+    """Y = [sigmoid(gate) * O~] W_o^T (gate before the projection); either part optional."""
+    d_model = o_tilde.shape[-1]
+    if gate is not None and gate.shape != o_tilde.shape:
+        raise ValueError("gate must have O~'s shape")
+    if w_o is not None and w_o.shape != (d_model, d_model):
+        raise ValueError("w_o must be [d_model, d_model]")
+    for t in (o_tilde, w_o, gate):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("gate_out takes contiguous tensors")
+    dev = _dev(o_tilde, w_o, gate)
+    _same_dtype(o_tilde, w_o, gate)
+    M = o_tilde.numel() // d_model
+    Y = torch.empty_like(o_tilde)
+    st = _lib.load().gmla_gate_out(_dtype(o_tilde), M, d_model, _ptr(gate), _ptr(o_tilde), _ptr(w_o),
+                                   _ptr(Y), _stream(dev, stream))
+    _lib.check(st, "gmla_gate_out")
+    return Y
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, *, out: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """x [..., K] times w [N, K] transposed -> [..., N]."""
+    K = x.shape[-1]
+    N = w.shape[0]
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError("w must be [N, K] with K = x.shape[-1]")
+    if not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("linear takes contiguous tensors")
+    dev = _dev(x, w, out)
+    _same_dtype(x, w, out)
+    M = x.numel() // K
+    if out is None:
+        out = torch.empty((*x.shape[:-1], N), dtype=x.dtype, device=dev)
+    elif out.shape != (*x.shape[:-1], N) or not out.is_contiguous():
+        raise ValueError("out has the wrong shape")
+    st = _lib.load().gmla_linear(_dtype(x), M, N, K, _ptr(x), _ptr(w), _ptr(out),
+                                 _stream(dev, stream))
+    _lib.check(st, "gmla_linear")
+    return out
+
+
+def gated_mla(hidden_states: torch.Tensor, query_projection: torch.Tensor,
+              latent_down_projection: torch.Tensor, key_up_projection: torch.Tensor,
+              value_up_projection: torch.Tensor, output_gate_projection: torch.Tensor,
+              output_projection: torch.Tensor, num_heads: int, causal: bool = True,
+              *, stream=None) -> dict:
+    """One Gated MLA layer ("Gated MLA", sections "Implementation order" and
+    "Requirements"): returns {"output": Y, "latent_cache": C} with Y shaped like the
+    hidden states and C [batch, sequence, latent width]; inputs are not modified.
+
+    Order: Q = X W_q^T, C = X W_c^T, [K | V] = C [W_k | W_v]^T, G = X W_g^T,
+    O~ = sigmoid(G) * attention(Q, K, V) (gate fused in the attention epilogue),
+    Y = O~ W_o^T.
+    """
+    if not isinstance(causal, bool):
+        raise TypeError("causal must be a bool")
+    if not isinstance(num_heads, int) or num_heads <= 0:
+        raise ValueError("num_heads must be a positive int")
+    X = hidden_states
+    if X.dim() != 3:
+        raise ValueError("hidden_states must be [batch, sequence, model width]")
+    B, T, dm = X.shape
+    if dm % num_heads:
+        raise ValueError("model width must be divisible by the head count")
+    ws = (query_projection, latent_down_projection, key_up_projection, value_up_projection,
+          output_gate_projection, output_projection)
+    _dev(X, *ws)
+    _same_dtype(X, *ws)
+    d_c = latent_down_projection.shape[0]
+    if (query_projection.shape != (dm, dm) or latent_down_projection.shape != (d_c, dm)
+            or key_up_projection.shape != (dm, d_c) or value_up_projection.shape != (dm, d_c)
+            or output_gate_projection.shape != (dm, dm) or output_projection.shape != (dm, dm)):
+        raise ValueError("projection matrices have incompatible widths")
+    D = dm // num_heads
+    X = X.contiguous()
+    Q = linear(X, query_projection, stream=stream)
+    C = linear(X, latent_down_projection, stream=stream)
+    K, V = latent_expand(C, key_up_projection, value_up_projection, stream=stream)
+    G = linear(X, output_gate_projection, stream=stream)
+    O = attend_prefill(Q.view(B, T, num_heads, D), K.view(B, T, num_heads, D),
+                       V.view(B, T, num_heads, D), G, causal=causal, stream=stream)
+    Y = gate_out(O, output_projection, stream=stream)
+    return {"output": Y, "latent_cache": C}

@@ -11,6 +11,7 @@ from .oracle import (  # noqa: F401
     attend,
     attend_head,
     build,
+    default_threads,
     gate,
     gated_mla_layer,
     library_path,

@@ -32,6 +32,16 @@ def library_path() -> str:
     return _LIB
 
 
+def default_threads() -> int:
+    """Threads the oracle uses when asked for 0: the CPUs this process may run on,
+    at most 16 (a GPU host's share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def build(src: str = _SRC, out: str = _LIB, force: bool = True) -> str:
     """Compile the oracle with gcc into a shared library; returns its path.
 
@@ -108,6 +118,7 @@ def attend_head(q, k, v, scale: float, causal: bool, rows=None, want_lse: bool =
     out = np.empty((n, D), dtype=np.float64)
     lse = np.empty(n, dtype=np.float64) if want_lse else None
     probs = np.empty((n, Tk), dtype=np.float64) if want_probs else None
+    nthreads = nthreads or default_threads()
     rc = lib.gmla_oracle_attend_head(
         Tq, Tk, D, float(scale), 1 if causal else 0,
         _ptr(q), q.strides[0] // 8, _ptr(k), k.strides[0] // 8, _ptr(v), v.strides[0] // 8,
@@ -166,6 +177,7 @@ def linear(X, W, nthreads: int = 0, lib=None) -> np.ndarray:
         raise ValueError("linear: inner widths differ")
     M = int(np.prod(lead)) if lead else 1
     Y = np.empty((M, N), dtype=np.float64)
+    nthreads = nthreads or default_threads()
     rc = lib.gmla_oracle_linear(M, N, K, _ptr(X), _ptr(W), _ptr(Y), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle linear failed (rc={rc})")

@@ -1,0 +1,126 @@
+"""GPU invariants that need no oracle: facts of the softmax definition that must hold
+exactly (or to the output rounding) for any correct kernel."""
+import numpy as np
+import pytest
+import torch
+
+import causal_softmax_attention_gmla_amd as gm
+from causal_softmax_attention_gmla_amd import inputs as I
+from gpu_helpers import announce, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+BF16_ULP = 2.0 ** -8
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_constant_values_give_constant_output(dtype, D):
+    """V = c on every key gives O = c: the weights of each row sum to one."""
+    dev = need_gpu()
+    announce(f"invariant constant V {dtype}")
+    q, k, _, _ = I.prefill_inputs(2, 333, 3, D, dtype, dev, seed=6000)
+    v = torch.full_like(q, 1.0)
+    out = host(gm.attend_prefill(q, k, v))
+    assert np.max(np.abs(out - 1.0)) <= (BF16_ULP if dtype == torch.bfloat16 else 1e-6)
+    kd = k.permute(0, 2, 1, 3)
+    dec = host(gm.attend_decode(q[:, -1].contiguous(), kd, torch.full_like(kd, 1.0), num_splits=3))
+    assert np.max(np.abs(dec - 1.0)) <= (BF16_ULP if dtype == torch.bfloat16 else 1e-6)
+
+
+def test_identity_values_reveal_causal_weights():
+    """V rows = unit vectors e_s (T <= 128 = D): output row t is A[t, :], whose upper
+    triangle must be exactly zero and whose rows sum to one."""
+    dev = need_gpu()
+    announce("invariant identity V")
+    T, D = 100, 128
+    q, k, _, _ = I.prefill_inputs(1, T, 2, D, torch.bfloat16, dev, seed=6100)
+    v = torch.zeros_like(q)
+    for s in range(T):
+        v[0, s, :, s] = 1.0
+    A = host(gm.attend_prefill(q, k, v)).reshape(T, 2, D)[:, :, :T]
+    for h in range(2):
+        assert np.all(np.triu(A[:, h], 1) == 0.0)
+        assert np.all(np.tril(A[:, h]) >= 0.0)
+        assert np.max(np.abs(A[:, h].sum(axis=1) - 1.0)) <= 2e-2
+
+
+def test_future_keys_do_not_change_past_rows_bitwise():
+    """Changing K and V at positions s > t0 leaves every output row t <= t0 bitwise
+    unchanged (keys after the query are removed before normalisation)."""
+    dev = need_gpu()
+    announce("invariant causal bitwise")
+    B, T, H, D = 1, 390, 2, 128
+    q, k, v, _ = I.prefill_inputs(B, T, H, D, torch.bfloat16, dev, seed=6200)
+    a = gm.attend_prefill(q, k, v).clone()
+    t0 = 200
+    k2, v2 = k.clone(), v.clone()
+    k2[:, t0 + 1:] = (I.normal(k2[:, t0 + 1:].shape, torch.float32, dev, seed=6201) * 8).to(k.dtype)
+    v2[:, t0 + 1:] = -5.0
+    b = gm.attend_prefill(q, k2, v2)
+    assert torch.equal(a[:, : t0 + 1], b[:, : t0 + 1])
+    assert not torch.equal(a[:, t0 + 1:], b[:, t0 + 1:])
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 32)])
+def test_first_row_is_first_value_bitwise(dtype, D):
+    """Query 0 sees only key 0: its weight is exactly 1 and the output is V[0]."""
+    dev = need_gpu()
+    announce(f"invariant first row {dtype}")
+    q, k, v, _ = I.prefill_inputs(2, 77, 3, D, dtype, dev, seed=6300)
+    out = gm.attend_prefill(q, k, v)
+    assert torch.equal(out[:, 0], v[:, 0].reshape(2, 3 * D))
+    one = gm.attend_prefill(q[:, :1].contiguous(), k[:, :1].contiguous(), v[:, :1].contiguous())
+    assert torch.equal(one[:, 0], v[:, 0].reshape(2, 3 * D))
+
+
+def test_zero_query_gives_prefix_mean():
+    """Q = 0: equal scores, uniform weights, output = causal prefix mean of V."""
+    dev = need_gpu()
+    announce("invariant zero query")
+    B, T, H, D = 1, 300, 2, 128
+    _, k, v, _ = I.prefill_inputs(B, T, H, D, torch.bfloat16, dev, seed=6400)
+    q = torch.zeros_like(k)
+    out = host(gm.attend_prefill(q, k, v)).reshape(B, T, H, D)
+    vh = host(v)
+    ref = np.cumsum(vh, axis=1) / np.arange(1, T + 1)[None, :, None, None]
+    err = np.abs(out - ref).max(axis=-1) / np.abs(ref).max(axis=-1)
+    assert np.max(err) <= 2e-2
+
+
+def test_decode_split_counts_agree():
+    """The log-sum-exp merge is an exact regrouping: any split count gives the same
+    result up to float32 rounding (checked in fp32)."""
+    dev = need_gpu()
+    announce("invariant decode splits")
+    q, k, v, _ = I.decode_inputs(2, 4, 3000, 128, torch.float32, dev, seed=6500)
+    outs = [host(gm.attend_decode(q, k, v, num_splits=s)) for s in (1, 2, 5, 16, 0)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-6
+
+
+def test_repeated_runs_bitwise_identical():
+    dev = need_gpu()
+    announce("invariant determinism")
+    q, k, v, g = I.prefill_inputs(2, 600, 4, 128, torch.bfloat16, dev, seed=6600, gate=True)
+    a = gm.attend_prefill(q, k, v, g).clone()
+    for _ in range(3):
+        assert torch.equal(gm.attend_prefill(q, k, v, g), a)
+    qd, kd, vd, _ = I.decode_inputs(4, 8, 5000, 128, torch.bfloat16, dev, seed=6601)
+    d = gm.attend_decode(qd, kd, vd).clone()
+    for _ in range(3):
+        assert torch.equal(gm.attend_decode(qd, kd, vd), d)
+
+
+def test_inputs_not_mutated():
+    """'Gated MLA', 'Requirements': no input tensor is modified."""
+    dev = need_gpu()
+    announce("invariant inputs unchanged")
+    q, k, v, g = I.prefill_inputs(1, 130, 2, 128, torch.bfloat16, dev, seed=6700, gate=True)
+    saved = [t.clone() for t in (q, k, v, g)]
+    gm.attend_prefill(q, k, v, g)
+    qd, kd, vd, gd = I.decode_inputs(1, 2, 700, 128, torch.bfloat16, dev, seed=6701, gate=True)
+    saved_d = [t.clone() for t in (qd, kd, vd, gd)]
+    gm.attend_decode(qd, kd, vd, gd, num_splits=3)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip((q, k, v, g), saved))
+    assert all(torch.equal(a, b) for a, b in zip((qd, kd, vd, gd), saved_d))

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the same
+seeded inputs, at sizes the oracle finishes in seconds that span several tiles and a
+ragged tail, plus the edge cases of the method."""
+import numpy as np
+import pytest
+import torch
+
+import causal_softmax_attention_gmla_amd as gm
+import oracle
+from causal_softmax_attention_gmla_amd import inputs as I
+from gpu_helpers import announce, check_f32_abs, check_rows_rel, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_prefill(q, k, v, g, causal, scale=None):
+    """Oracle output [B, T, H*D] (gated if g is given) from device tensors' bytes."""
+    B, T, H, D = q.shape
+    scale = scale if scale is not None else 1.0 / np.sqrt(D)
+    o = oracle.attend(host(q), host(k), host(v), scale, causal, layout="bthd").reshape(B, T, H * D)
+    if g is not None:
+        o = oracle.gate(host(g), o)
+    return o
+
+
+# ---------------------------------------------------------------- prefill
+
+
+def test_tiny_prefill_f32_gated():
+    """Causal prefill B=1 T=64 H=4 D=32 fp32, gated, against the oracle at 1e-5."""
+    dev = need_gpu()
+    announce("tiny_prefill_f32 gated")
+    q, k, v, g = I.workload_inputs("tiny_prefill_f32", dev)
+    out = gm.attend_prefill(q, k, v, g)
+    torch.cuda.synchronize()
+    ref = _oracle_prefill(q, k, v, g, True)
+    check_f32_abs(host(out), ref)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("T", [1, 5, 64, 65, 130])
+def test_prefill_f32_shapes(T, D):
+    dev = need_gpu()
+    announce(f"prefill f32 T={T} D={D}")
+    q, k, v, g = I.prefill_inputs(2, T, 3, D, torch.float32, dev, seed=1000 + T + D, gate=True)
+    for causal in (True, False):
+        out = gm.attend_prefill(q, k, v, g, causal=causal)
+        torch.cuda.synchronize()
+        check_f32_abs(host(out), _oracle_prefill(q, k, v, g, causal))
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 300, 517])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_bf16_mfma_shapes(T, causal):
+    """The MFMA kernel (D = 128) across tile boundaries and ragged tails."""
+    dev = need_gpu()
+    announce(f"prefill bf16 D=128 T={T} causal={causal}")
+    q, k, v, g = I.prefill_inputs(2, T, 3, 128, torch.bfloat16, dev, seed=2000 + T, gate=(T % 2 == 1))
+    out = gm.attend_prefill(q, k, v, g, causal=causal)
+    torch.cuda.synchronize()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, g, causal), 128)
+
+
+@pytest.mark.parametrize("D", [32, 64])
+def test_prefill_bf16_small_heads(D):
+    dev = need_gpu()
+    announce(f"prefill bf16 D={D}")
+    q, k, v, g = I.prefill_inputs(1, 200, 4, D, torch.bfloat16, dev, seed=2500 + D, gate=True)
+    out = gm.attend_prefill(q, k, v, g)
+    torch.cuda.synchronize()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, g, True), D)
+
+
+def test_prefill_bf16_strided_views():
+    """Q, K, V as head views into one packed [B, T, 3, H, D] buffer (strides != contiguous)."""
+    dev = need_gpu()
+    announce("prefill bf16 strided views")
+    B, T, H, D = 2, 257, 4, 128
+    qkv = I.normal((B, T, 3, H, D), torch.bfloat16, dev, seed=2600)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    out = gm.attend_prefill(q, k, v)
+    torch.cuda.synchronize()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, None, True), 128)
+
+
+def test_prefill_bf16_large_scores():
+    """Scores far from N(0,1) (inputs x 4: scaled-score std ~ 16) still follow the
+    plain softmax: the lazy rescale must keep the weights exact."""
+    dev = need_gpu()
+    announce("prefill bf16 large scores")
+    q, k, v, _ = I.prefill_inputs(1, 400, 2, 128, torch.bfloat16, dev, seed=2700)
+    q = (q.float() * 4).to(torch.bfloat16)
+    k = (k.float() * 4).to(torch.bfloat16)
+    out = gm.attend_prefill(q, k, v)
+    torch.cuda.synchronize()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, None, True), 128)
+
+
+def test_prefill_three_token_pattern():
+    """The three-token example ('Gated MLA', 'A small causal example'): with V the
+    identity on the first three channels, output row t reveals A[t, :], which must be
+    lower-triangular with A[0] = (1, 0, 0) exactly."""
+    dev = need_gpu()
+    announce("prefill three-token pattern")
+    for dtype, D in ((torch.bfloat16, 128), (torch.float32, 32)):
+        q, k, _, _ = I.prefill_inputs(1, 3, 1, D, dtype, dev, seed=2800)
+        v = torch.zeros((1, 3, 1, D), dtype=dtype, device=dev)
+        for s in range(3):
+            v[0, s, 0, s] = 1.0
+        A = host(gm.attend_prefill(q, k, v))[0, :, :3]
+        assert A[0, 0] == 1.0 and A[0, 1] == 0.0 and A[0, 2] == 0.0
+        assert A[1, 2] == 0.0 and A[1, 0] > 0 and A[1, 1] > 0
+        assert np.all(A[2] > 0)
+        assert np.allclose(A.sum(axis=1), 1.0, atol=1e-2)
+
+
+# ---------------------------------------------------------------- decode
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 7])
+def test_decode_b8_n1001(splits):
+    """Decode at the pages' shape (B=8, H=96, 1001 keys, bf16), every head against the oracle."""
+    dev = need_gpu()
+    announce(f"decode_b8_n1001 splits={splits}")
+    q, k, v, _ = I.workload_inputs("decode_b8_n1001", dev)
+    out = gm.attend_decode(q, k, v, num_splits=splits)
+    torch.cuda.synchronize()
+    B, H, N, D = k.shape
+    ref = oracle.attend(host(q)[:, :, None, :], host(k), host(v), 1 / np.sqrt(D), True,
+                        layout="bhtd").reshape(B, H * D)
+    check_rows_rel(host(out), ref, D)
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 255, 256, 257, 1000])
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (128, torch.float32),
+                                     (64, torch.bfloat16), (32, torch.float32)])
+def test_decode_shapes(N, D, dtype):
+    dev = need_gpu()
+    announce(f"decode N={N} D={D} {dtype}")
+    q, k, v, g = I.decode_inputs(2, 3, N, D, dtype, dev, seed=3000 + N + D, gate=True)
+    ref = oracle.attend(host(q)[:, :, None, :], host(k), host(v), 1 / np.sqrt(D), True,
+                        layout="bhtd").reshape(2, 3 * D)
+    ref = oracle.gate(host(g), ref)
+    for splits in (0, 1, 3):
+        out = gm.attend_decode(q, k, v, g, num_splits=splits)
+        torch.cuda.synchronize()
+        if dtype == torch.float32:
+            check_f32_abs(host(out), ref)
+        else:
+            check_rows_rel(host(out), ref, D)
+
+
+def test_decode_token_major_cache():
+    """K, V stored [B, N, H, D] (token-major) and passed as strided [B, H, N, D] views."""
+    dev = need_gpu()
+    announce("decode token-major cache")
+    B, N, H, D = 2, 333, 4, 128
+    kt = I.normal((B, N, H, D), torch.bfloat16, dev, seed=3100)
+    vt = I.normal((B, N, H, D), torch.bfloat16, dev, seed=3101)
+    q = I.normal((B, H, D), torch.bfloat16, dev, seed=3102)
+    k, v = kt.permute(0, 2, 1, 3), vt.permute(0, 2, 1, 3)
+    out = gm.attend_decode(q, k, v, num_splits=2)
+    torch.cuda.synchronize()
+    ref = oracle.attend(host(q)[:, :, None, :], host(k), host(v), 1 / np.sqrt(D), True,
+                        layout="bhtd").reshape(B, H * D)
+    check_rows_rel(host(out), ref, D)
+
+
+def test_decode_matches_prefill_last_row():
+    """decode(query t against keys 0..t) equals row t of the causal prefill."""
+    dev = need_gpu()
+    announce("decode vs prefill last row")
+    B, T, H, D = 1, 200, 2, 128
+    q, k, v, _ = I.prefill_inputs(B, T, H, D, torch.bfloat16, dev, seed=3200)
+    pre = host(gm.attend_prefill(q, k, v))[:, -1]
+    dec = host(gm.attend_decode(q[:, -1].contiguous(), k.permute(0, 2, 1, 3),
+                                v.permute(0, 2, 1, 3)))
+    check_rows_rel(dec, pre, D)
+
+
+# ---------------------------------------------------------------- projections
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (77, 200, 64), (130, 256, 136), (256, 384, 512)])
+def test_linear(M, N, K, dtype):
+    dev = need_gpu()
+    announce(f"linear {M}x{N}x{K} {dtype}")
+    x = I.normal((M, K), dtype, dev, seed=4000 + M)
+    w = I.normal((N, K), dtype, dev, seed=4001 + N, std=K ** -0.5)
+    y = gm.linear(x, w)
+    torch.cuda.synchronize()
+    ref = oracle.linear(host(x), host(w))
+    if dtype == torch.float32:
+        check_f32_abs(host(y), ref, 1e-4)
+    else:
+        check_rows_rel(host(y), ref, N)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_latent_expand(dtype):
+    dev = need_gpu()
+    announce(f"latent_expand {dtype}")
+    M, dc, dm = 150, 64, 384
+    c = I.normal((M, dc), dtype, dev, seed=4100)
+    wk = I.normal((dm, dc), dtype, dev, seed=4101, std=dc ** -0.5)
+    wv = I.normal((dm, dc), dtype, dev, seed=4102, std=dc ** -0.5)
+    K, V = gm.latent_expand(c, wk, wv)
+    torch.cuda.synchronize()
+    for got, w in ((K, wk), (V, wv)):
+        ref = oracle.linear(host(c), host(w))
+        if dtype == torch.float32:
+            check_f32_abs(host(got), ref, 1e-4)
+        else:
+            check_rows_rel(host(got), ref, dm)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("with_gate,with_proj", [(True, True), (True, False), (False, True)])
+def test_gate_out(dtype, with_gate, with_proj):
+    dev = need_gpu()
+    announce(f"gate_out {dtype} gate={with_gate} proj={with_proj}")
+    M, dm = 96, 256
+    o = I.normal((M, dm), dtype, dev, seed=4200)
+    g = I.normal((M, dm), dtype, dev, seed=4201) if with_gate else None
+    w = I.normal((dm, dm), dtype, dev, seed=4202, std=dm ** -0.5) if with_proj else None
+    y = gm.gate_out(o, w, g)
+    torch.cuda.synchronize()
+    ref = host(o)
+    if with_gate:
+        ref = oracle.gate(host(g), ref)
+    if with_proj:
+        ref = oracle.linear(ref, host(w))
+    if dtype == torch.float32:
+        check_f32_abs(host(y), ref, 1e-4)
+    else:
+        check_rows_rel(host(y), ref, dm)
+
+
+def test_gate_example_on_gpu():
+    """'Gated MLA', 'A small causal example': 1.6 with gate logit 0 becomes 0.8
+    (exact in fp32; in bf16, bf16(1.6)/2 = bf16(0.8))."""
+    dev = need_gpu()
+    announce("gate example")
+    for dtype in (torch.float32, torch.bfloat16):
+        o = torch.full((1, 8), 1.6, dtype=dtype, device=dev)
+        g = torch.zeros((1, 8), dtype=dtype, device=dev)
+        y = gm.gate_out(o, None, g)
+        assert torch.all(y == torch.tensor(0.8, dtype=dtype)).item()
+
+
+# ---------------------------------------------------------------- layer
+
+
+@pytest.mark.parametrize("dtype,dm,H,dc", [(torch.bfloat16, 256, 2, 64), (torch.float32, 128, 4, 32),
+                                           (torch.bfloat16, 384, 3, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gated_mla_layer_small(dtype, dm, H, dc, causal):
+    dev = need_gpu()
+    announce(f"gated_mla {dtype} dm={dm} H={H} dc={dc} causal={causal}")
+    B, T = 2, 100
+    x, ws = I.layer_inputs(B, T, dm, dc, dtype, dev, seed=5000 + dm)
+    saved = {n: w.clone() for n, w in ws.items()}
+    xs = x.clone()
+    res = gm.gated_mla(x, ws["Wq"], ws["Wc"], ws["Wk"], ws["Wv"], ws["Wg"], ws["Wo"], H, causal)
+    torch.cuda.synchronize()
+    assert set(res) == {"output", "latent_cache"}
+    assert res["output"].shape == x.shape and res["output"].dtype == x.dtype
+    assert res["latent_cache"].shape == (B, T, dc)
+    assert torch.equal(x, xs) and all(torch.equal(ws[n], saved[n]) for n in ws)
+    ref = oracle.gated_mla_layer(host(x), *(host(ws[n]) for n in ("Wq", "Wc", "Wk", "Wv", "Wg", "Wo")),
+                                 H, causal)
+    if dtype == torch.float32:
+        check_f32_abs(host(res["latent_cache"]), ref["latent_cache"], 1e-4)
+        check_f32_abs(host(res["output"]), ref["output"], 1e-4)
+    else:
+        check_rows_rel(host(res["latent_cache"]), ref["latent_cache"], dc)
+        check_rows_rel(host(res["output"]), ref["output"], dm)
+    other = gm.gated_mla(x, ws["Wq"], ws["Wc"], ws["Wk"], ws["Wv"], ws["Wg"], ws["Wo"], H, not causal)
+    assert torch.equal(other["latent_cache"], res["latent_cache"])
