@@ -76,6 +76,8 @@ int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int 
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
         (G && !aligned(G, 16)) || a.sb % 8 || a.st % 8 || a.sh % 8)
       return GMLA_ERR_INVALID_ARG;
+    // byte offsets inside one 64-token tile are 32-bit
+    if (a.st >= (int64_t)1 << 24) return GMLA_ERR_UNSUPPORTED;
     if (log_enabled())
       fprintf(stderr, "gmla: prefill bf16 mfma B=%d T=%d H=%d causal=%d gate=%d\n", B, T, H,
               causal, G != nullptr);

@@ -17,16 +17,22 @@
 //    (after f32 -> bf16 rounding): no shuffles.  O^T keeps each query's 128 output
 //    channels in that query's lanes, so rescaling by the running maximum is
 //    lane-local as well.
+//  * Software pipeline: keys run one tile ahead of values.  Iteration j turns the
+//    scores of tile j into weights while the MFMAs of the next tile's scores
+//    (K_{j+1} Q^T) and of this tile's values (V_j^T P_j^T) issue, so the vector
+//    ALU work of the softmax overlaps the matrix cores.
 //  * K tiles sit in LDS row-major; V tiles are written to LDS transposed (V^T), with
 //    the keys of every 16-key group permuted so that each A-operand fragment is one
-//    16-byte LDS read.  Both tiles are padded/swizzled to avoid bank conflicts, and
-//    double-buffered: the next tile's global loads are in flight during the MFMAs.
-//  * Online softmax in base 2 (scale * log2 e folded into one FMA); the running
-//    maximum is only raised when a tile's maximum exceeds it by more than 2^8, which
-//    skips most O rescales; the stale maximum only scales numerator and
+//    16-byte LDS read.  Row paddings make both the fragment reads and the transposing
+//    writes free of bank conflicts.  Two buffers each; one barrier per tile.
+//  * Global loads are buffer loads whose range ends at the last valid row: rows
+//    past the sequence end read as zero without any per-lane predicate.
+//  * Online softmax in base 2 (scale * log2 e folded into one FMA); a row's running
+//    maximum is only raised when the tile's maximum exceeds it by more than 2^8,
+//    which skips most O rescales; the stale maximum scales numerator and
 //    denominator alike, so the result is unchanged.
 //  * Causal tiles above the diagonal are never loaded; the mask is an index compare
-//    applied only on tiles that straddle the diagonal or the sequence end.
+//    applied only on the two tiles that straddle the diagonal or the sequence end.
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
 //    (shared L2), heaviest (longest-prefix) blocks first.
 #include "gmla_internal.h"
@@ -38,11 +44,12 @@ constexpr int HD = 128;         // head width
 constexpr int BM = 128;         // queries per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int NTHREADS = 256;   // 4 waves
-constexpr int K_LD = HD + 8;    // K tile row stride (bf16): 272 B rows, conflict-free reads
+constexpr int K_LD = HD + 8;    // K tile row stride (bf16): 272 B rows
 constexpr int VT_LD = BN + 8;   // V^T tile row stride (bf16): 144 B rows
 constexpr int K_TILE = BN * K_LD;
 constexpr int VT_TILE = HD * VT_LD;
-constexpr float kLazyRescale = 8.0f;  // raise the running max only past 2^8 growth
+constexpr float kLazyRescale = 8.0f;   // raise the running max only past 2^8 growth
+constexpr int kBufferDword3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
 struct __align__(16) Smem {
   bf16 k[2][K_TILE];
@@ -54,11 +61,6 @@ struct __align__(16) Smem {
 // O^T MFMA from its S^T accumulator registers (keys 4h..4h+3 and 8+4h..8+4h+3).
 __device__ __forceinline__ int key_group_slot(int g4) { return g4 == 1 ? 2 : (g4 == 2 ? 1 : g4); }
 
-// V^T element (d, slot) lives at d*VT_LD + ((slot/8) ^ ((d/16) & 7))*8 + slot%8.
-__device__ __forceinline__ int vt_offset(int d, int chunk) {
-  return d * VT_LD + ((chunk ^ ((d >> 4) & 7)) << 3);
-}
-
 __device__ __forceinline__ float swap_halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -66,6 +68,20 @@ __device__ __forceinline__ float swap_halves_max(float x) {
 __device__ __forceinline__ float swap_halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over rows [tile*BN, tile*BN + BN) of one head; rows at or past T
+// (and whole tiles past the end) fall outside its range and load as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* head, int tile, int T,
+                                                           int64_t st) {
+  const int rows = min(BN, T - tile * BN);
+  const int bytes = rows > 0 ? (int)(((int64_t)(rows - 1) * st + HD) * 2) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)tile * BN * st), (short)0, bytes,
+                                           kBufferDword3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb,
@@ -98,7 +114,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- this lane's query row and its Q fragments (B operand of S^T = K Q^T)
   const int wq0 = q0 + wave * 32;  // first query of this wave
   const int tq = wq0 + l32;        // this lane's query
-  const bool wave_active = wq0 < T;
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -111,45 +126,66 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- key tiles this workgroup visits
   const int nkt_all = (T + BN - 1) / BN;
   const int ntiles = a.causal ? min(nkt_all, (q0 + BM) / BN) : nkt_all;
-  const int wave_last_q = min(wq0 + 31, T - 1);
+  // first tile that needs the index mask: the diagonal pair (causal) or the tail
+  const int mask_from = a.causal ? ntiles - 2 : (T % BN ? ntiles - 1 : ntiles);
 
-  // global -> register staging of one K and one V tile (4 x 16 B each per thread)
-  u32x4 kreg[4], vreg[4];
-  const int v_kg = tid >> 4;  // key group of 4 keys (0..15)
-  const int v_c16 = tid & 15;  // 8-channel chunk of the value row
-  auto load_tile = [&](int tile) {
-    const int kbase = tile * BN;
+  // per-thread byte offsets of the staged rows inside a tile (constant per tile)
+  uint32_t koff[4], voff[4];
+  const int v_kg = tid & 15;   // value key group: keys 4*v_kg .. 4*v_kg+3
+  const int v_c16 = tid >> 4;  // value channel chunk: channels 8*v_c16 .. +7
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = i * NTHREADS + tid;
-      const int key = kbase + (id >> 4);
-      kreg[i] = key < T ? *(const u32x4*)(Kh + (int64_t)key * st + (id & 15) * 8) : u32x4{};
-      const int vkey = kbase + v_kg * 4 + i;
-      vreg[i] = vkey < T ? *(const u32x4*)(Vh + (int64_t)vkey * st + v_c16 * 8) : u32x4{};
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int id = i * NTHREADS + tid;
+    koff[i] = (uint32_t)(((id >> 4) * st + (id & 15) * 8) * 2);
+    voff[i] = (uint32_t)(((v_kg * 4 + i) * st + v_c16 * 8) * 2);
+  }
+  const int vt_slot = (v_kg >> 2) * 16 + key_group_slot(v_kg & 3) * 4;
+
+  u32x4 kreg[4], vreg[4];
+  auto load_k = [&](int tile) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kh, tile, T, st);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kreg[i] = buffer_load16(r, koff[i]);
   };
-  auto store_tile = [&](int buf) {
+  auto load_v = [&](int tile) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vh, tile, T, st);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vreg[i] = buffer_load16(r, voff[i]);
+  };
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int id = i * NTHREADS + tid;
       *(u32x4*)(&sm.k[buf][(id >> 4) * K_LD + (id & 15) * 8]) = kreg[i];
     }
-    // transpose 4 keys x 8 channels into 8 channels x 4 keys (8-byte LDS writes)
-    const int g16 = v_kg >> 2;
-    const int gs = key_group_slot(v_kg & 3);
-    const int chunk = g16 * 2 + (gs >> 1);
-    const int within = (gs & 1) * 4;
+  };
+  // transpose 4 keys x 8 channels into 8 channels x 4 keys (8-byte LDS writes); the
+  // 16 lanes that share a channel chunk write one full 128-byte V^T row
+  auto store_v = [&](int buf) {
+    bf16* base = &sm.vt[buf][(v_c16 * 8) * VT_LD + vt_slot];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-      const int d = v_c16 * 8 + 2 * w;
       u32x2 even, odd;
       even[0] = (x0 & 0xffffu) | (x1 << 16);
       even[1] = (x2 & 0xffffu) | (x3 << 16);
       odd[0] = (x0 >> 16) | (x1 & 0xffff0000u);
       odd[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-      *(u32x2*)(&sm.vt[buf][vt_offset(d, chunk) + within]) = even;
-      *(u32x2*)(&sm.vt[buf][vt_offset(d + 1, chunk) + within]) = odd;
+      *(u32x2*)(base + (2 * w) * VT_LD) = even;
+      *(u32x2*)(base + (2 * w + 1) * VT_LD) = odd;
+    }
+  };
+  // S^T = K Q^T for the 64 keys of a K buffer (two 32-key halves)
+  auto scores = [&](int buf, f32x16* s) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      s[sub] = f32x16{};
+      const bf16* krow = &sm.k[buf][(sub * 32 + l32) * K_LD + hh * 8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(krow + ks * 16);
+        s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[sub], 0, 0, 0);
+      }
     }
   };
 
@@ -163,94 +199,93 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   bf16x2 ones2;
   ones2[0] = (bf16)1.0f;
   ones2[1] = (bf16)1.0f;
+  const int lim = a.causal ? min(tq, T - 1) : T - 1;  // last key this query may see
 
-  load_tile(0);
-  store_tile(0);
+  // ---- prologue: K0, V0 and K1 in LDS; scores of tile 0
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  load_k(1);
+  store_k(1);
   __syncthreads();
+  f32x16 s_cur[2];
+  scores(0, s_cur);
+  __syncthreads();  // every wave has read K buffer 0 before iteration 0 refills it
 
   for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    // next loads in flight: K two tiles ahead, V one tile ahead (zero past the end)
+    load_k(j + 2);
+    load_v(j + 1);
 
     const int kbase = j * BN;
-    if (wave_active && kbase <= (a.causal ? wave_last_q : T - 1)) {
-      // S^T = K Q^T for two 32-key halves of the tile
-      f32x16 s[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        s[sub] = f32x16{};
-        const bf16* krow = &sm.k[buf][(sub * 32 + l32) * K_LD + hh * 8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 kf = *(const bf16x8*)(krow + ks * 16);
-          s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[sub], 0, 0, 0);
-        }
-      }
-      // mask keys after the query (causal) or past the sequence end
-      const bool diag = a.causal ? (kbase + BN - 1 > wq0) : false;
-      if (diag || kbase + BN > T) {
-        const int lim = a.causal ? min(tq, T - 1) : T - 1;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim) s[sub][r] = -INFINITY;
-          }
-      }
-      // tile maximum of this query (both halves)
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = swap_halves_max(mx);
-      const float mt = mx * c2;
-      const bool grow = mt > m_run + kLazyRescale;
-      if (__any(grow)) {
-        // only the lanes whose maximum grew move it; the others keep theirs
-        // exactly (alpha = 1), so a row never depends on its neighbours' scores
-        const float alpha = grow ? fast_exp2(m_run - mt) : 1.0f;  // m_run = -inf: 0
-        m_run = grow ? mt : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o_acc[i][r] *= alpha;
-      }
-      // weights, rounded to bf16 as the B operand of O^T = V^T P^T
-      bf16x8 p[2][2];
+    if (j >= mask_from) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[sub][half * 8 + e], c2, -m_run));
-            const float p1 = fast_exp2(__builtin_fmaf(s[sub][half * 8 + e + 1], c2, -m_run));
-            bf16x2 pp;
-            pp[0] = (bf16)p0;
-            pp[1] = (bf16)p1;
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
-            p[sub][half][e] = pp[0];
-            p[sub][half][e + 1] = pp[1];
-          }
-      // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16), 4 blocks of 32 channels
-#pragma unroll
-      for (int kstep = 0; kstep < 4; ++kstep) {
-        const bf16x8 pb = p[kstep >> 1][kstep & 1];
-        const int chunk = kstep * 2 + hh;
-#pragma unroll
-        for (int dblk = 0; dblk < 4; ++dblk) {
-          const int d = dblk * 32 + l32;
-          const bf16x8 vf = *(const bf16x8*)(&sm.vt[buf][vt_offset(d, chunk)]);
-          o_acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o_acc[dblk], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key > lim) s_cur[sub][r] = -INFINITY;
         }
+    }
+    // tile maximum of this query (both halves)
+    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s_cur[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[1][r]);
+    mx = swap_halves_max(mx);
+    const float mt = mx * c2;
+    const bool grow = mt > m_run + kLazyRescale;
+    if (__any(grow)) {
+      // only the lanes whose maximum grew move it; the others keep theirs
+      // exactly (alpha = 1), so a row never depends on its neighbours' scores
+      const float alpha = grow ? fast_exp2(m_run - mt) : 1.0f;  // m_run = -inf: 0
+      m_run = grow ? mt : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o_acc[i][r] *= alpha;
+    }
+    // weights, rounded to bf16 as the B operand of O^T = V^T P^T
+    bf16x8 p[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s_cur[sub][half * 8 + e], c2, -m_run));
+          const float p1 = fast_exp2(__builtin_fmaf(s_cur[sub][half * 8 + e + 1], c2, -m_run));
+          bf16x2 pp;
+          pp[0] = (bf16)p0;
+          pp[1] = (bf16)p1;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
+          p[sub][half][e] = pp[0];
+          p[sub][half][e + 1] = pp[1];
+        }
+    // scores of the next tile (its K is already in LDS)
+    f32x16 s_next[2];
+    scores((j + 1) & 1, s_next);
+    // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16), 4 blocks of 32 channels
+    const int vb = j & 1;
+#pragma unroll
+    for (int kstep = 0; kstep < 4; ++kstep) {
+      const bf16x8 pb = p[kstep >> 1][kstep & 1];
+#pragma unroll
+      for (int dblk = 0; dblk < 4; ++dblk) {
+        const bf16x8 vf =
+            *(const bf16x8*)(&sm.vt[vb][(dblk * 32 + l32) * VT_LD + (kstep * 2 + hh) * 8]);
+        o_acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o_acc[dblk], 0, 0, 0);
       }
     }
-
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    // stage K_{j+2} (into the buffer K_j used) and V_{j+1}
+    store_k(j & 1);
+    store_v((j + 1) & 1);
     __syncthreads();
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
   }
 
   // ---- epilogue: normalise, gate, round, store [B, T, H*128]
