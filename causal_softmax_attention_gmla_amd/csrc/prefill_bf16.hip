@@ -21,12 +21,15 @@
 //    scores of tile j into weights while the MFMAs of the next tile's scores
 //    (K_{j+1} Q^T) and of this tile's values (V_j^T P_j^T) issue, so the vector
 //    ALU work of the softmax overlaps the matrix cores.
-//  * K tiles sit in LDS row-major; V tiles are written to LDS transposed (V^T), with
-//    the keys of every 16-key group permuted so that each A-operand fragment is one
-//    16-byte LDS read.  Row paddings make both the fragment reads and the transposing
-//    writes free of bank conflicts.  Two buffers each; one barrier per tile.
-//  * Global loads are buffer loads whose range ends at the last valid row: rows
-//    past the sequence end read as zero without any per-lane predicate.
+//  * K and V tiles go from global memory straight into LDS (buffer loads with the
+//    LDS-direct form: no register staging, no vector ALU work).  Each load range ends
+//    at the last valid row, so rows past the sequence end arrive as zeros with no
+//    per-lane predicate.  Both tiles are row-major with the 16-byte chunks of each row
+//    XOR-swizzled so that the fragment reads are free of bank conflicts.
+//  * The value operand is read with the transposing LDS load ds_read_b64_tr_b16:
+//    each 16-lane group gathers 16 consecutive channels of 4 keys, which is exactly
+//    the A-operand layout of O^T = V^T P^T for the keys the lane's P^T registers hold.
+//    Two buffers per tile kind; one barrier per tile.
 //  * Online softmax in base 2 (scale * log2 e folded into one FMA); a row's running
 //    maximum is only raised when the tile's maximum exceeds it by more than 2^8,
 //    which skips most O rescales; the stale maximum scales numerator and
@@ -35,6 +38,8 @@
 //    applied only on the two tiles that straddle the diagonal or the sequence end.
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
 //    (shared L2), heaviest (longest-prefix) blocks first.
+#include <type_traits>
+
 #include "gmla_internal.h"
 
 namespace gmla {
@@ -44,22 +49,28 @@ constexpr int HD = 128;         // head width
 constexpr int BM = 128;         // queries per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int NTHREADS = 256;   // 4 waves
-constexpr int K_LD = HD + 8;    // K tile row stride (bf16): 272 B rows
-constexpr int VT_LD = BN + 8;   // V^T tile row stride (bf16): 144 B rows
-constexpr int K_TILE = BN * K_LD;
-constexpr int VT_TILE = HD * VT_LD;
+constexpr int TILE = BN * HD;   // bf16 elements of one K or V tile (16 KB)
 constexpr float kLazyRescale = 8.0f;   // raise the running max only past 2^8 growth
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
-struct __align__(16) Smem {
-  bf16 k[2][K_TILE];
-  bf16 vt[2][VT_TILE];
-};
+// One array per buffer, so that the compiler can tell an LDS-direct load into one
+// buffer from reads of another and does not wait for the load before those reads.
+__shared__ __align__(16) bf16 lds_k0[TILE];
+__shared__ __align__(16) bf16 lds_k1[TILE];
+__shared__ __align__(16) bf16 lds_v0[TILE];
+__shared__ __align__(16) bf16 lds_v1[TILE];
+template <int B> __device__ __forceinline__ bf16* k_buf() { return B ? lds_k1 : lds_k0; }
+template <int B> __device__ __forceinline__ bf16* v_buf() { return B ? lds_v1 : lds_v0; }
 
-// Key slot inside a 16-key group of the V^T tile: keys 4..7 and 8..11 trade places,
-// so that slots 8h .. 8h+7 hold exactly the keys that lane half h feeds to the
-// O^T MFMA from its S^T accumulator registers (keys 4h..4h+3 and 8+4h..8+4h+3).
-__device__ __forceinline__ int key_group_slot(int g4) { return g4 == 1 ? 2 : (g4 == 2 ? 1 : g4); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// Swizzles of the 16-byte chunk index (8 channels) inside a 256-byte tile row.
+// K: 16 consecutive rows read the same logical chunk -> 16 distinct bank groups.
+// V: the transposing reads of one lane half touch 4 consecutive rows x 4 chunks.
+__device__ __forceinline__ int k_chunk(int row, int c) { return c ^ (row & 15); }
+__device__ __forceinline__ int v_chunk(int row, int c) { return c ^ ((row & 3) << 2); }
 
 __device__ __forceinline__ float swap_halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -80,13 +91,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* head, in
                                            kBufferDword3);
 }
 
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+// 64 lanes x 16 bytes from global (lane's own byte offset) into 1 KB of LDS at dst,
+// lane i's bytes landing at dst + 16 i.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, bf16* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, off, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb,
                                                                    int total) {
-  __shared__ Smem sm;
 
   // ---- workgroup -> (head, query block): same-head blocks on one XCD, heavy first
   const int bid = blockIdx.x;
@@ -129,65 +141,63 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // first tile that needs the index mask: the diagonal pair (causal) or the tail
   const int mask_from = a.causal ? ntiles - 2 : (T % BN ? ntiles - 1 : ntiles);
 
-  // per-thread byte offsets of the staged rows inside a tile (constant per tile)
+  // Tile staging: each wave moves 4 KB of a tile (4 loads of 64 lanes x 16 bytes).
+  // Load u of wave w fills LDS rows 4m .. 4m+3 (m = 4w + u) in physical chunk order;
+  // lane i therefore fetches row 4m + i/16, logical chunk (i mod 16) ^ swizzle(row).
   uint32_t koff[4], voff[4];
-  const int v_kg = tid & 15;   // value key group: keys 4*v_kg .. 4*v_kg+3
-  const int v_c16 = tid >> 4;  // value channel chunk: channels 8*v_c16 .. +7
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = i * NTHREADS + tid;
-    koff[i] = (uint32_t)(((id >> 4) * st + (id & 15) * 8) * 2);
-    voff[i] = (uint32_t)(((v_kg * 4 + i) * st + v_c16 * 8) * 2);
+  for (int u = 0; u < 4; ++u) {
+    const int row = 4 * (wave * 4 + u) + (lane >> 4);
+    koff[u] = (uint32_t)((row * st + k_chunk(row, lane & 15) * 8) * 2);
+    voff[u] = (uint32_t)((row * st + v_chunk(row, lane & 15) * 8) * 2);
   }
-  const int vt_slot = (v_kg >> 2) * 16 + key_group_slot(v_kg & 3) * 4;
-
-  u32x4 kreg[4], vreg[4];
-  auto load_k = [&](int tile) {
+  auto load_k = [&](int tile, auto buf) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kh, tile, T, st);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = buffer_load16(r, koff[i]);
+    for (int u = 0; u < 4; ++u)
+      load_lds16(r, k_buf<decltype(buf)::value>() + (wave * 4 + u) * 512, koff[u]);
   };
-  auto load_v = [&](int tile) {
+  auto load_v = [&](int tile, auto buf) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vh, tile, T, st);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = buffer_load16(r, voff[i]);
+    for (int u = 0; u < 4; ++u)
+      load_lds16(r, v_buf<decltype(buf)::value>() + (wave * 4 + u) * 512, voff[u]);
   };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = i * NTHREADS + tid;
-      *(u32x4*)(&sm.k[buf][(id >> 4) * K_LD + (id & 15) * 8]) = kreg[i];
-    }
-  };
-  // transpose 4 keys x 8 channels into 8 channels x 4 keys (8-byte LDS writes); the
-  // 16 lanes that share a channel chunk write one full 128-byte V^T row
-  auto store_v = [&](int buf) {
-    bf16* base = &sm.vt[buf][(v_c16 * 8) * VT_LD + vt_slot];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-      u32x2 even, odd;
-      even[0] = (x0 & 0xffffu) | (x1 << 16);
-      even[1] = (x2 & 0xffffu) | (x3 << 16);
-      odd[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-      odd[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-      *(u32x2*)(base + (2 * w) * VT_LD) = even;
-      *(u32x2*)(base + (2 * w + 1) * VT_LD) = odd;
-    }
+  // wait for this wave's LDS-direct loads, then for every wave
+  auto tile_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
   // S^T = K Q^T for the 64 keys of a K buffer (two 32-key halves)
-  auto scores = [&](int buf, f32x16* s) {
+  auto scores = [&](auto buf, f32x16* s) __attribute__((always_inline)) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       s[sub] = f32x16{};
-      const bf16* krow = &sm.k[buf][(sub * 32 + l32) * K_LD + hh * 8];
+      const int row = sub * 32 + l32;
+      const bf16* krow = k_buf<decltype(buf)::value>() + row * HD;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(krow + ks * 16);
+        const bf16x8 kf = *(const bf16x8*)(krow + k_chunk(row, ks * 2 + hh) * 8);
         s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[sub], 0, 0, 0);
       }
     }
   };
+
+  // Transposed value reads: in each 16-lane group (lane p = lane mod 16) lane p points
+  // at key 4*hh + p/4 (and that + 8), channels dbase + 4*(p mod 4) .. +3, with dbase =
+  // 32*dblk + 16*((lane/16) mod 2); the hardware then hands lane p channel dbase + p
+  // of those 4 keys: keys 16*kstep + 4*hh + {0..3, 8..11} for channel 32*dblk + (lane
+  // mod 32), matching the keys of this lane's P^T registers.
+  int v_off[4];
+  {
+    const int p = lane & 15;
+    const int row = 4 * hh + (p >> 2);
+#pragma unroll
+    for (int dblk = 0; dblk < 4; ++dblk) {
+      const int d0 = dblk * 32 + 16 * ((lane >> 4) & 1) + 4 * (p & 3);
+      v_off[dblk] = row * HD + v_chunk(row, d0 >> 3) * 8 + (d0 & 7);
+    }
+  }
 
   // ---- accumulators
   f32x16 o_acc[4];
@@ -201,53 +211,71 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   ones2[1] = (bf16)1.0f;
   const int lim = a.causal ? min(tq, T - 1) : T - 1;  // last key this query may see
 
-  // ---- prologue: K0, V0 and K1 in LDS; scores of tile 0
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  load_k(1);
-  store_k(1);
-  __syncthreads();
+  // keys after the query (causal) or past the sequence end score -inf
+  auto mask = [&](f32x16* s, int tile) __attribute__((always_inline)) {
+    const int kbase = tile * BN;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key > lim) s[sub][r] = -INFINITY;
+      }
+  };
+  // this query's maximum over a tile (both lane halves), in base-2 units
+  auto tile_max = [&](const f32x16* s) __attribute__((always_inline)) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    return swap_halves_max(mx) * c2;
+  };
+
+  // ---- prologue: K0, V0 and K1 in LDS; scores and maximum of tile 0
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  load_k(0, B0{});
+  load_v(0, B0{});
+  load_k(1, B1{});
+  tile_barrier();
   f32x16 s_cur[2];
-  scores(0, s_cur);
+  scores(B0{}, s_cur);
+  if (0 >= mask_from) mask(s_cur, 0);
+  float mt_cur = tile_max(s_cur);
   __syncthreads();  // every wave has read K buffer 0 before iteration 0 refills it
 
-  for (int j = 0; j < ntiles; ++j) {
-    // next loads in flight: K two tiles ahead, V one tile ahead (zero past the end)
-    load_k(j + 2);
-    load_v(j + 1);
-
-    const int kbase = j * BN;
-    if (j >= mask_from) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > lim) s_cur[sub][r] = -INFINITY;
-        }
-    }
-    // tile maximum of this query (both halves)
-    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s_cur[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[1][r]);
-    mx = swap_halves_max(mx);
-    const float mt = mx * c2;
-    const bool grow = mt > m_run + kLazyRescale;
+  // One iteration: weights of tile j, values of tile j, scores of tile j+1.
+  //   NEXT: 0 = there is a next tile (masked if it straddles the diagonal or the end),
+  //         2 = tile j is the last one.
+  //   PAR = j mod 2 selects the buffers: K_{j+1} and V_j are read, K_{j+2} and V_{j+1}
+  //   are loaded into the buffers K_j and V_{j-1} used.
+  auto step = [&](int j, auto next_kind, auto parity) __attribute__((always_inline)) {
+    constexpr int NEXT = decltype(next_kind)::value;
+    constexpr int PAR = decltype(parity)::value;
+    using BP = std::integral_constant<int, PAR>;
+    using BQ = std::integral_constant<int, 1 - PAR>;
+    const bool grow = mt_cur > m_run + kLazyRescale;
     if (__any(grow)) {
       // only the lanes whose maximum grew move it; the others keep theirs
       // exactly (alpha = 1), so a row never depends on its neighbours' scores
-      const float alpha = grow ? fast_exp2(m_run - mt) : 1.0f;  // m_run = -inf: 0
-      m_run = grow ? mt : m_run;
+      const float alpha = grow ? fast_exp2(m_run - mt_cur) : 1.0f;  // m_run = -inf: 0
+      m_run = grow ? mt_cur : m_run;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[i][r] *= alpha;
     }
+    if (NEXT != 2) {
+      // next tiles in flight straight into LDS: K two tiles ahead (into the buffer K_j
+      // used), V one tile ahead; tiles past the end arrive as zeros
+      load_k(j + 2, BP{});
+      load_v(j + 1, BQ{});
+    }
+    // scores of the next tile (its K is already in LDS)
+    f32x16 s_next[2];
+    if (NEXT != 2) scores(BQ{}, s_next);
     // weights, rounded to bf16 as the B operand of O^T = V^T P^T
     bf16x8 p[2][2];
 #pragma unroll
@@ -265,27 +293,41 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
           p[sub][half][e] = pp[0];
           p[sub][half][e + 1] = pp[1];
         }
-    // scores of the next tile (its K is already in LDS)
-    f32x16 s_next[2];
-    scores((j + 1) & 1, s_next);
     // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16), 4 blocks of 32 channels
-    const int vb = j & 1;
+    const bf16* vtile = v_buf<PAR>();
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const bf16x8 pb = p[kstep >> 1][kstep & 1];
 #pragma unroll
       for (int dblk = 0; dblk < 4; ++dblk) {
-        const bf16x8 vf =
-            *(const bf16x8*)(&sm.vt[vb][(dblk * 32 + l32) * VT_LD + (kstep * 2 + hh) * 8]);
+        const bf16* src = vtile + kstep * 16 * HD + v_off[dblk];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src + 8 * HD));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o_acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o_acc[dblk], 0, 0, 0);
       }
     }
-    // stage K_{j+2} (into the buffer K_j used) and V_{j+1}
-    store_k(j & 1);
-    store_v((j + 1) & 1);
-    __syncthreads();
-    s_cur[0] = s_next[0];
-    s_cur[1] = s_next[1];
+    if (NEXT != 2) {
+      if (j + 1 >= mask_from) mask(s_next, j + 1);
+      mt_cur = tile_max(s_next);
+      tile_barrier();
+      s_cur[0] = s_next[0];
+      s_cur[1] = s_next[1];
+    }
+  };
+
+  using NotLast = std::integral_constant<int, 0>;
+  using Last = std::integral_constant<int, 2>;
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {  // j even: buffers alternate with the parity of j
+    step(j, NotLast{}, B0{});
+    step(j + 1, NotLast{}, B1{});
+  }
+  if (j + 1 < ntiles) {
+    step(j, NotLast{}, B0{});
+    step(j + 1, Last{}, B1{});
+  } else {
+    step(j, Last{}, B0{});
   }
 
   // ---- epilogue: normalise, gate, round, store [B, T, H*128]
