@@ -11,10 +11,21 @@ against 1001 keys, B=8 H=96 D=128 bf16, algorithmic bytes K + V + Q + O) is the
 kernels run on, over exactly K timed calls after W warm-up calls.  ``roofline``
 compares the dominant kernel with MI355X's published peaks; ``cpu_baseline`` times
 the plain CPU oracle on a bounded sample of the same workload.
+
+Profiling helpers (no compute of their own):
+    python bench.py --only prefill|decode|layer|decode_long|copy --steps K
+        run just that part, for rocprofv3 --kernel-trace or --pmc passes;
+    python bench.py --summarize-stats DIR --name NAME --cmd "..."
+        turn rocprofv3 kernel statistics in DIR into profiles/NAME.md;
+    python bench.py --summarize-traffic DIR_FETCH DIR_WRITE COPY_FETCH COPY_WRITE --kernel K --cmd "..."
+        turn FETCH_SIZE / WRITE_SIZE passes (kernel and a 1 GiB copy for scale)
+        into the entry for kernel K in profiles/traffic.json.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import math
@@ -26,7 +37,17 @@ METRIC = "causal attn TFLOP/s prefill T=4096; decode HBM GB/s at 1001 keys"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+PROFILES = os.path.join(HERE, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+COPY_BYTES = 1 << 30
+
+# sources of each timed kernel: its traffic record is valid only for these bytes
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": ["causal_softmax_attention_gmla_amd/csrc/prefill_bf16.hip",
+                            "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"],
+    "decode_split_kernel": ["causal_softmax_attention_gmla_amd/csrc/decode.hip",
+                            "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"],
+}
 
 
 def prefill_flops(B, T, H, D):
@@ -39,23 +60,23 @@ def decode_bytes(B, H, N, D, elem=2):
     return (2 * B * H * N * D + 2 * B * H * D) * elem
 
 
-def source_digest(files):
+def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in files:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(HERE, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, files):
-    """HBM bytes per launch from committed rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs,
-    only if the kernel source is unchanged since they were taken."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    passes, only if the kernel source is unchanged since they were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != source_digest(files):
+    if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -94,17 +115,16 @@ def cpu_prefill_baseline(q, k, v, budget_s=12.0):
         qh = q[b, :, h].float().cpu().numpy()
         kh = k[b, :, h].float().cpu().numpy()
         vh = v[b, :, h].float().cpu().numpy()
-        ts = time.perf_counter()
         oracle.attend_head(qh, kh, vh, 1.0 / math.sqrt(D), True, nthreads=threads)
         done_flops += prefill_flops(1, T, 1, D)
         heads += 1
         if time.perf_counter() - t0 > budget_s or heads >= B * H:
             break
-        _ = ts
     el = time.perf_counter() - t0
-    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done_flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"{heads} of {B * H} heads (all {T} query rows each) of the prefill workload, "
-                      f"{el:.1f} s, float64, {threads} threads"}
+                      f"{el:.1f} s including host copies, float64, {threads} threads"}
 
 
 def cpu_decode_baseline(q, k, v, budget_s=6.0):
@@ -128,9 +148,108 @@ def cpu_decode_baseline(q, k, v, budget_s=6.0):
         if time.perf_counter() - t0 > budget_s or heads >= 4 * B * H:
             break
     el = time.perf_counter() - t0
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} (batch, head) decode rows of 1001 keys, {el:.1f} s, float64, 1 thread "
-                      f"(one query row cannot be split across threads by the oracle)"}
+    return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} (batch, head) decode rows of {N} keys, {el:.1f} s, float64, 1 thread "
+                      f"(the oracle runs one query row on one thread)"}
+
+
+# ----------------------------------------------------------------------------- profiles
+
+
+def _read_csvs(d, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name: str) -> str:
+    name = name.split("(")[0]
+    return name if len(name) < 90 else name[:87] + "..."
+
+
+def summarize_stats(d, name, cmd):
+    rows = _read_csvs(d, "kernel_stats.csv")
+    if not rows:
+        sys.exit(f"no *kernel_stats.csv under {d}")
+    lines = [f"# {name}", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share (%) |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r.get("Percentage", 0))):
+        ns = lambda k: float(r.get(k, "nan")) / 1e3  # noqa: E731
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {ns('AverageNs'):.1f} | "
+                     f"{ns('MinNs'):.1f} | {ns('MaxNs'):.1f} | {float(r['Percentage']):.2f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def _counter_per_dispatch(d, counter, match):
+    vals = {}
+    for r in _read_csvs(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter or match not in r["Kernel_Name"]:
+            continue
+        key = r["Dispatch_Id"]
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        sys.exit(f"no {counter} for {match} under {d}")
+    ordered = [vals[k] for k in sorted(vals, key=int)]
+    return ordered[-1], len(ordered)  # last dispatch: warm caches, steady state
+
+
+def summarize_traffic(d_fetch, d_write, c_fetch, c_write, kernel, cmd):
+    kf, _ = _counter_per_dispatch(d_fetch, "FETCH_SIZE", kernel)
+    kw, _ = _counter_per_dispatch(d_write, "WRITE_SIZE", kernel)
+    cf, _ = _counter_per_dispatch(c_fetch, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_per_dispatch(c_write, "WRITE_SIZE", "copyBuffer")
+    # each counter reads in KiB; a plain copy of COPY_BYTES fixes its scale
+    fetch_scale = COPY_BYTES / (cf * 1024.0)
+    write_scale = COPY_BYTES / (cw * 1024.0)
+    fetch = kf * 1024.0 * fetch_scale
+    write = kw * 1024.0 * write_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[kernel] = {"source_digest": source_digest(kernel), "bytes_per_launch": round(fetch + write),
+                    "fetch_bytes": round(fetch), "write_bytes": round(write),
+                    "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+                    "raw_fetch_kib": kf, "raw_write_kib": kw, "copy_fetch_kib": cf,
+                    "copy_write_kib": cw, "command": cmd}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(data[kernel]))
+
+
+def summarize_counters(d, kernel, name, cmd):
+    """Every counter of the last dispatch of `kernel` in a --pmc pass, as a table."""
+    vals, last = {}, None
+    for r in _read_csvs(d, "counter_collection.csv"):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        did = int(r["Dispatch_Id"])
+        if last is None or did > last:
+            last, vals = did, {}
+        if did == last:
+            vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        sys.exit(f"no counters for {kernel} under {d}")
+    lines = [f"# {name}", "", f"Counters of the last dispatch of `{kernel}` (dispatch {last}).", "",
+             "Command:", "", "```", cmd, "```", "", "| counter | value |", "|---|---|"]
+    lines += [f"| {k} | {v:.6g} |" for k, v in sorted(vals.items())]
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+# ----------------------------------------------------------------------------- main
 
 
 def main():
@@ -141,7 +260,20 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the layer and the 131072-key decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-splits", type=int, default=0)
+    ap.add_argument("--only", choices=["prefill", "decode", "layer", "decode_long", "copy"])
+    ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--name")
+    ap.add_argument("--kernel")
+    ap.add_argument("--cmd", default="")
     args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats, args.name, args.cmd)
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic, args.kernel, args.cmd)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.kernel, args.name, args.cmd)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               f"sharding is described, not built.", file=sys.stderr)
@@ -158,94 +290,110 @@ def main():
     gm.library()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     K, W = args.steps, args.warmup
+    only = args.only
+
+    if only == "copy":  # scale reference for the FETCH_SIZE / WRITE_SIZE counters
+        a = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(max(K, 1)):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": max(K, 1)}))
+        return
+
+    result = {"metric": METRIC, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic"}
 
     # ---------------- prefill: B=2 T=4096 H=96 D=128 bf16, causal
-    pw = I.WORKLOADS["prefill_b2_t4096"]
-    d = pw.dims
-    q, k, v, _ = I.workload_inputs(pw.name, dev)
-    out = torch.empty((d["B"], d["T"], d["H"] * d["D"]), dtype=q.dtype, device=dev)
-    flops = prefill_flops(d["B"], d["T"], d["H"], d["D"])
-    ms, wall = time_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), K, W)
-    avg = sum(ms) / len(ms)
-    tflops = flops / (avg * 1e-3) / 1e12
-    pre_files = ["causal_softmax_attention_gmla_amd/csrc/prefill_bf16.hip",
-                 "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"]
-    result = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": round(wall * 1e3 / K, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": pw.name, "B": d["B"], "T": d["T"], "H": d["H"], "D": d["D"],
-                   "causal": True, "inputs": "N(0,1) rounded to bf16, seeded"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_bf16_kernel", pre_files),
-                     "kernel": "prefill_bf16_kernel", "algorithmic_flop_per_launch": flops,
-                     "avg_launch_ms": round(avg, 4), "min_launch_ms": round(min(ms), 4)},
-    }
+    q = k = v = None
+    if only in (None, "prefill"):
+        pw = I.WORKLOADS["prefill_b2_t4096"]
+        d = pw.dims
+        q, k, v, _ = I.workload_inputs(pw.name, dev)
+        out = torch.empty((d["B"], d["T"], d["H"] * d["D"]), dtype=q.dtype, device=dev)
+        flops = prefill_flops(d["B"], d["T"], d["H"], d["D"])
+        ms, wall = time_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), K, W)
+        avg = sum(ms) / len(ms)
+        tflops = flops / (avg * 1e-3) / 1e12
+        result.update({
+            "value": round(tflops, 2), "ms_per_step": round(wall * 1e3 / K, 4),
+            "config": {"workload": pw.name, "B": d["B"], "T": d["T"], "H": d["H"], "D": d["D"],
+                       "causal": True, "inputs": "N(0,1) rounded to bf16, seeded"},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_bf16_kernel"),
+                         "kernel": "prefill_bf16_kernel", "algorithmic_flop_per_launch": flops,
+                         "avg_launch_ms": round(avg, 4), "min_launch_ms": round(min(ms), 4)},
+        })
 
     # ---------------- decode: B=8 H=96 N=1001 D=128 bf16, rotated over 4 input sets
-    dw = I.WORKLOADS["decode_b8_n1001"]
-    dd = dw.dims
-    sets = []
-    for r in range(4):
-        qd, kd, vd, _ = I.decode_inputs(dd["B"], dd["H"], dd["N"], dd["D"], dw.dtype, dev,
-                                        seed=I.seed_of(dw.name) + 10 * r)
-        sets.append((qd, kd, vd, torch.empty((dd["B"], dd["H"] * dd["D"]), dtype=dw.dtype,
-                                             device=dev)))
-    splits = args.decode_splits or gm.decode_num_splits(dd["B"], dd["H"], dd["N"], dd["D"])
-    wsb = gm.decode_workspace_bytes(dd["B"], dd["H"], dd["N"], dd["D"], splits)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-    nbytes = decode_bytes(dd["B"], dd["H"], dd["N"], dd["D"])
+    sets = None
+    if only in (None, "decode"):
+        dw = I.WORKLOADS["decode_b8_n1001"]
+        dd = dw.dims
+        sets = []
+        for r in range(4):
+            qd, kd, vd, _ = I.decode_inputs(dd["B"], dd["H"], dd["N"], dd["D"], dw.dtype, dev,
+                                            seed=I.seed_of(dw.name) + 10 * r)
+            sets.append((qd, kd, vd, torch.empty((dd["B"], dd["H"] * dd["D"]), dtype=dw.dtype,
+                                                 device=dev)))
+        splits = args.decode_splits or gm.decode_num_splits(dd["B"], dd["H"], dd["N"], dd["D"])
+        wsb = gm.decode_workspace_bytes(dd["B"], dd["H"], dd["N"], dd["D"], splits)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        nbytes = decode_bytes(dd["B"], dd["H"], dd["N"], dd["D"])
 
-    def dec(i):
-        qd, kd, vd, od = sets[i]
-        gm.attend_decode(qd, kd, vd, num_splits=splits, workspace=ws, out=od)
+        def dec(i):
+            qd, kd, vd, od = sets[i]
+            gm.attend_decode(qd, kd, vd, num_splits=splits, workspace=ws, out=od)
 
-    dms, dwall = time_calls(torch, dec, max(K, 20), W, rotate=4)
-    davg = sum(dms) / len(dms)
-    gbps = nbytes / (davg * 1e-3) / 1e9
-    dec_files = ["causal_softmax_attention_gmla_amd/csrc/decode.hip",
-                 "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"]
-    result["decode"] = {
-        "workload": dw.name, "value": round(gbps, 1), "unit": "GB/s", "splits": splits,
-        "calls": len(dms), "avg_call_ms": round(davg, 5), "min_call_ms": round(min(dms), 5),
-        "rotation": "4 input sets (1.58 GB) cycled so the 256 MB last-level cache cannot hold them",
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic("decode_split_kernel", dec_files),
-                     "kernel": "decode_split_kernel (+ decode_merge_kernel when splits > 1)",
-                     "algorithmic_bytes_per_call": nbytes},
-    }
+        dms, dwall = time_calls(torch, dec, max(K, 20), W, rotate=4)
+        davg = sum(dms) / len(dms)
+        gbps = nbytes / (davg * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": dw.name, "value": round(gbps, 1), "unit": "GB/s", "splits": splits,
+            "calls": len(dms), "avg_call_ms": round(davg, 5), "min_call_ms": round(min(dms), 5),
+            "rotation": "4 input sets (1.58 GB) cycled so the 256 MB last-level cache cannot hold them",
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                         "traffic": measured_traffic("decode_split_kernel"),
+                         "kernel": "decode_split_kernel" + (" + decode_merge_kernel" if splits > 1 else ""),
+                         "algorithmic_bytes_per_call": nbytes},
+        }
+        if only == "decode":
+            result.update({"value": round(gbps, 1), "unit": "GB/s",
+                           "ms_per_step": round(dwall * 1e3 / len(dms), 4)})
 
-    if args.all:
+    if args.all or only in ("layer", "decode_long"):
         extra = {}
-        # full layer B=1 T=2048 d_model=12288 d_c=512
-        lw = I.WORKLOADS["layer_t2048"]
-        ld = lw.dims
-        x, wts = I.workload_inputs(lw.name, dev)
-        lms, _ = time_calls(torch, lambda i: gm.gated_mla(x, wts["Wq"], wts["Wc"], wts["Wk"], wts["Wv"],
-                                                          wts["Wg"], wts["Wo"], ld["H"], True),
-                            max(5, K // 5), 2)
-        T_, dm, dc = ld["T"], ld["d_model"], ld["d_c"]
-        lflops = 2 * T_ * (3 * dm * dm + 3 * dm * dc) + prefill_flops(1, T_, ld["H"], dm // ld["H"])
-        lavg = sum(lms) / len(lms)
-        extra[lw.name] = {"value": round(lflops / (lavg * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
-                          "avg_call_ms": round(lavg, 4), "algorithmic_flop": lflops}
-        del x, wts
-        # long decode B=4 H=96 N=131072
-        cw = I.WORKLOADS["decode_b4_n131072"]
-        cd = cw.dims
-        qc, kc, vc, _ = I.workload_inputs(cw.name, dev)
-        cms, _ = time_calls(torch, lambda i: gm.attend_decode(qc, kc, vc), max(5, K // 5), 2)
-        cavg = sum(cms) / len(cms)
-        cb = decode_bytes(cd["B"], cd["H"], cd["N"], cd["D"])
-        extra[cw.name] = {"value": round(cb / (cavg * 1e-3) / 1e9, 1), "unit": "GB/s",
-                          "avg_call_ms": round(cavg, 4), "algorithmic_bytes": cb,
-                          "splits": gm.decode_num_splits(cd["B"], cd["H"], cd["N"], cd["D"])}
-        del qc, kc, vc
+        if only in (None, "layer"):
+            lw = I.WORKLOADS["layer_t2048"]
+            ld = lw.dims
+            x, wts = I.workload_inputs(lw.name, dev)
+            lms, _ = time_calls(torch, lambda i: gm.gated_mla(x, wts["Wq"], wts["Wc"], wts["Wk"],
+                                                              wts["Wv"], wts["Wg"], wts["Wo"],
+                                                              ld["H"], True),
+                                max(5, K // 5), 2)
+            T_, dm, dc = ld["T"], ld["d_model"], ld["d_c"]
+            lflops = 2 * T_ * (3 * dm * dm + 3 * dm * dc) + prefill_flops(1, T_, ld["H"], dm // ld["H"])
+            lavg = sum(lms) / len(lms)
+            extra[lw.name] = {"value": round(lflops / (lavg * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                              "avg_call_ms": round(lavg, 4), "algorithmic_flop": lflops}
+            del x, wts
+        if only in (None, "decode_long"):
+            cw = I.WORKLOADS["decode_b4_n131072"]
+            cd = cw.dims
+            qc, kc, vc, _ = I.workload_inputs(cw.name, dev)
+            cms, _ = time_calls(torch, lambda i: gm.attend_decode(qc, kc, vc), max(5, K // 5), 2)
+            cavg = sum(cms) / len(cms)
+            cb = decode_bytes(cd["B"], cd["H"], cd["N"], cd["D"])
+            extra[cw.name] = {"value": round(cb / (cavg * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "avg_call_ms": round(cavg, 4), "algorithmic_bytes": cb,
+                              "splits": gm.decode_num_splits(cd["B"], cd["H"], cd["N"], cd["D"])}
+            del qc, kc, vc
         result["extra"] = extra
 
-    if not args.no_cpu:
+    if not args.no_cpu and only is None:
         result["cpu_baseline"] = cpu_prefill_baseline(q, k, v)
         qd, kd, vd, _ = sets[0]
         result["decode"]["cpu_baseline"] = cpu_decode_baseline(qd, kd, vd)

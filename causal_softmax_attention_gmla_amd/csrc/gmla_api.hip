@@ -93,11 +93,13 @@ int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int 
 int gmla_decode_num_splits(int B, int H, int N, int D) {
   (void)D;
   if (B <= 0 || H <= 0 || N <= 0) return 1;
-  // Enough workgroups to cover the 256 compute units several times over, but
-  // never a split shorter than 256 keys.
+  // Enough workgroups to cover the 256 compute units about eight times over, but
+  // never a split shorter than 1024 keys: for short caches (one head = a few hundred
+  // KB) the cross-split merge costs more than the extra parallelism gains.
   const long heads = (long)B * H;
   long splits = (2048 + heads - 1) / heads;
-  const long max_by_len = (N + 255) / 256;
+  long max_by_len = N / 1024;
+  if (max_by_len < 1) max_by_len = 1;
   if (splits > max_by_len) splits = max_by_len;
   if (splits < 1) splits = 1;
   if (splits > 256) splits = 256;

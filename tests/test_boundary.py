@@ -97,7 +97,10 @@ def test_decode_split_heuristic():
     lib = gm.library()
     for B, H, N in ((8, 96, 1001), (4, 96, 131072), (1, 1, 1), (1, 1, 100000), (64, 96, 50)):
         s = lib.gmla_decode_num_splits(B, H, N, 128)
-        assert 1 <= s <= 256 and s <= max(1, (N + 255) // 256)
+        assert 1 <= s <= 256 and s <= max(1, N // 1024)
+    # the two decode workloads: one split for 1001 keys, six for 131072 keys
+    assert lib.gmla_decode_num_splits(8, 96, 1001, 128) == 1
+    assert lib.gmla_decode_num_splits(4, 96, 131072, 128) == 6
 
 
 def test_projection_argument_checks():
