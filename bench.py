@@ -165,7 +165,7 @@ def _read_csvs(d, suffix):
 
 
 def _short(name: str) -> str:
-    name = name.split("(")[0]
+    name = name.replace("(anonymous namespace)", "{anon}").split("(")[0]
     return name if len(name) < 90 else name[:87] + "..."
 
 
