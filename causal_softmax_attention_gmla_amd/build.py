@@ -20,7 +20,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgmla.so")
 ARCH = "gfx950"
 
-SOURCES = ["gmla_api.hip", "prefill_bf16.hip", "prefill_simple.hip", "decode.hip", "gemm.hip"]
+SOURCES = ["gmla_api.hip", "prefill_bf16.hip", "prefill_simple.hip", "decode.hip", "gemm.hip", "gemm_lds.hip"]
 
 # -packed-fp32-ops: never emit packed float32 VALU instructions (v_pk_fma_f32 and
 # friends); the host pass prints a harmless "not a recognized feature" warning.

@@ -200,6 +200,7 @@ __global__ __launch_bounds__(256) void gate_kernel(int64_t n, const T* g, const 
 }  // namespace
 
 hipError_t launch_gemm(int dtype, const GemmArgs& p, hipStream_t s) {
+  if (dtype == 1 && gemm_lds_supported(p)) return launch_gemm_lds(p, s);
   if (dtype == 1) {
     const int nb1 = (p.N + GBN - 1) / GBN;
     const int nb2 = p.w2 ? (p.N2 + GBN - 1) / GBN : 0;

@@ -1,0 +1,320 @@
+// Y = X W^T for bf16 X [M, K], W [N, K] (both contiguous along K), f32 accumulation,
+// bf16 output: the dense projections of a Gated MLA layer ("Gated MLA", sections
+// "Start from familiar attention" and "The channel-wise output gate": Q = X W_q^T,
+// C = X W_c^T, K = C W_k^T, V = C W_v^T, G = X W_g^T, Y = O~ W_o^T).
+//
+// Design (gfx950):
+//  * Tiles of X (BM rows) and W (BN rows) x 64 k move from global memory straight into
+//    LDS with the LDS-direct form of the buffer load (no register staging), S stages
+//    deep, so a stage is requested S-1 stages before it is used.  The buffer range of
+//    a tile ends at the last valid row: rows past M (or N) load as zeros, with no
+//    per-lane predicate.  Each stage is its own __shared__ array and the stage loop is
+//    unrolled by S, so the compiler sees that a load into one stage does not alias the
+//    reads of another (it would otherwise wait for every load before any LDS read).
+//  * LDS rows are 128 bytes (64 k); the 16-byte chunk c of row r sits at chunk
+//    c ^ ((r >> 1) & 7), which makes the fragment reads free of bank conflicts.
+//  * The MFMA computes D = W X^T (v_mfma_f32_32x32x16_bf16, A = 32 rows of W, B = 32
+//    rows of X): a lane then holds four consecutive output columns n of one output row
+//    m per register quad, so results leave as 8-byte stores.
+//  * Workgroups are dealt so that the M blocks of one N block run on the same XCD:
+//    the W tile they share is fetched from HBM once into that XCD's L2.
+#include <type_traits>
+
+#include "gmla_internal.h"
+
+namespace gmla {
+namespace {
+
+constexpr int BK = 64;                 // k per stage: one 128-byte LDS row
+constexpr int kBufferDword3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Hides a value from loop-invariant code motion, so address arithmetic derived from it
+// is redone at each use (one VALU op) instead of occupying registers across the loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// s_waitcnt vmcnt(N) (N < 64) leaving the other counters alone.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Barrier for the LDS stages: the caller has waited (vmcnt) for the loads the next
+// stage reads; this waits for the wave's own LDS reads and meets the other waves.  A
+// __syncthreads() would also wait for the loads meant to stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int S, int WGM, int WGN>
+struct Cfg {
+  static constexpr int NW = WGM * WGN;          // waves
+  static constexpr int NT = NW * 64;            // threads
+  static constexpr int TM = BM / WGM;           // wave tile (rows of X)
+  static constexpr int TN = BN / WGN;           // wave tile (rows of W)
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int XL = BM / 8 / NW;        // 1 KB loads per wave per stage (X)
+  static constexpr int WL = BN / 8 / NW;        // (W)
+  static constexpr int LPS = XL + WL;           // loads per wave per stage
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(XL >= 1 && WL >= 1 && XL * NW * 8 == BM && WL * NW * 8 == BN, "load split");
+  static_assert(S >= 2 && S <= 4, "stages");
+};
+
+// Stage buffers, one set per tile shape.  They live at namespace scope (not inside the
+// kernel) so that each is a distinct LDS object to the compiler's alias analysis; a
+// kernel is allocated only the buffers it references.
+__shared__ __align__(16) bf16 wide_x0[256 * BK];
+__shared__ __align__(16) bf16 wide_x1[256 * BK];
+__shared__ __align__(16) bf16 wide_x2[256 * BK];
+__shared__ __align__(16) bf16 wide_w0[128 * BK];
+__shared__ __align__(16) bf16 wide_w1[128 * BK];
+__shared__ __align__(16) bf16 wide_w2[128 * BK];
+__shared__ __align__(16) bf16 narrow_x0[64 * BK];
+__shared__ __align__(16) bf16 narrow_x1[64 * BK];
+__shared__ __align__(16) bf16 narrow_x2[64 * BK];
+__shared__ __align__(16) bf16 narrow_x3[64 * BK];
+__shared__ __align__(16) bf16 narrow_w0[64 * BK];
+__shared__ __align__(16) bf16 narrow_w1[64 * BK];
+__shared__ __align__(16) bf16 narrow_w2[64 * BK];
+__shared__ __align__(16) bf16 narrow_w3[64 * BK];
+
+template <int BM, int BN, int S> struct StageSet;
+template <> struct StageSet<256, 128, 3> {
+  template <int B> static __device__ __forceinline__ bf16* x() {
+    return B == 0 ? wide_x0 : B == 1 ? wide_x1 : wide_x2;
+  }
+  template <int B> static __device__ __forceinline__ bf16* w() {
+    return B == 0 ? wide_w0 : B == 1 ? wide_w1 : wide_w2;
+  }
+};
+template <> struct StageSet<64, 64, 4> {
+  template <int B> static __device__ __forceinline__ bf16* x() {
+    return B == 0 ? narrow_x0 : B == 1 ? narrow_x1 : B == 2 ? narrow_x2 : narrow_x3;
+  }
+  template <int B> static __device__ __forceinline__ bf16* w() {
+    return B == 0 ? narrow_w0 : B == 1 ? narrow_w1 : B == 2 ? narrow_w2 : narrow_w3;
+  }
+};
+
+template <int BM, int BN, int S, int WGM, int WGN>
+__device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nmb, int total) {
+  using C = Cfg<BM, BN, S, WGM, WGN>;
+  auto xbuf = [&](auto b) __attribute__((always_inline)) -> bf16* {
+    constexpr int B = decltype(b)::value;
+    return StageSet<BM, BN, S>::template x<B>();
+  };
+  auto wbuf = [&](auto b) __attribute__((always_inline)) -> bf16* {
+    constexpr int B = decltype(b)::value;
+    return StageSet<BM, BN, S>::template w<B>();
+  };
+
+  // ---- workgroup -> (m block, n block); the m blocks of one n block share an XCD
+  const int bid = blockIdx.x;
+  const int per_xcd = total / kNumXcd;
+  const int L = bid < per_xcd * kNumXcd ? (bid % kNumXcd) * per_xcd + bid / kNumXcd : bid;
+  const int mb = L % nmb;
+  int nblk = L / nmb;
+  const bf16* W = (const bf16*)p.w;
+  bf16* Y = (bf16*)p.y;
+  int N = p.N;
+  if (nblk >= nb1) {
+    nblk -= nb1;
+    W = (const bf16*)p.w2;
+    Y = (bf16*)p.y2;
+    N = p.N2;
+  }
+  const int M = p.M, K = p.K;
+  const int m0 = mb * BM, n0 = nblk * BN;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = wave % WGM, wn = wave / WGM;
+
+  // ---- buffer resources over this block's rows of X and W
+  const int xrows = min(BM, M - m0), wrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16*)p.x + (int64_t)m0 * K), (short)0, xrows * K * 2, kBufferDword3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * K), (short)0, wrows * K * 2, kBufferDword3);
+
+  // Load u of a wave fills 8 LDS rows (1 KB) in physical chunk order: lane i writes
+  // row 8 (wave * L + u) + i / 8, physical chunk i mod 8, i.e. logical chunk
+  // (i mod 8) ^ ((row >> 1) & 7) of that row; the stage's k offset is the scalar part.
+  uint32_t xo[C::XL], wo[C::WL];
+#pragma unroll
+  for (int u = 0; u < C::XL; ++u) {
+    const int row = 8 * (wave * C::XL + u) + (lane >> 3);
+    xo[u] = (uint32_t)(row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
+  }
+#pragma unroll
+  for (int u = 0; u < C::WL; ++u) {
+    const int row = 8 * (wave * C::WL + u) + (lane >> 3);
+    wo[u] = (uint32_t)(row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
+  }
+  auto load_stage = [&](int kt, auto b) __attribute__((always_inline)) {
+    const int koff = kt * BK * 2;
+#pragma unroll
+    for (int u = 0; u < C::XL; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(xbuf(b) + (wave * C::XL + u) * 512),
+                                               16, xo[u], koff, 0, 0);
+#pragma unroll
+    for (int u = 0; u < C::WL; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t*)(wbuf(b) + (wave * C::WL + u) * 512),
+                                               16, wo[u], koff, 0, 0);
+  };
+
+  // Fragment reads: row l32 of a 32-row group, logical chunk 2 ks + hh, at byte
+  // (frag_lane ^ 32 ks) from the group's first row (the swizzle only moves bits 4..6).
+  const int frag_lane = l32 * 128 + ((hh ^ ((l32 >> 1) & 7)) << 4);
+
+  f32x16 acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+
+  auto compute = [&](auto b) __attribute__((always_inline)) {
+    const char* xt = (const char*)xbuf(b) + wm * C::TM * 128;
+    const char* wt = (const char*)wbuf(b) + wn * C::TN * 128;
+    const int fl = opaque(frag_lane);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 xf[C::FM], wf[C::FN];
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) xf[j] = *(const bf16x8*)(xt + j * 4096 + (fl ^ (ks << 5)));
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) wf[i] = *(const bf16x8*)(wt + i * 4096 + (fl ^ (ks << 5)));
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ---- pipeline: stage kt is requested at iteration kt - (S - 1)
+  const int nk = K / BK;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  load_stage(0, B0{});
+  if (S > 2 && nk > 1) load_stage(1, B1{});
+  if (S > 3 && nk > 2) load_stage(2, B2{});
+
+  // iteration kt: wait for stage kt (the S-2 later stages may stay in flight), barrier
+  // (every wave is done with stage kt-1, whose buffer the next request reuses),
+  // request stage kt+S-1, compute stage kt.  This general form serves the last stages.
+  auto step = [&](int kt, auto b) __attribute__((always_inline)) {
+    constexpr int Bc = decltype(b)::value;
+    const int ahead = min(nk - 1 - kt, S - 2);  // stages after kt already requested
+    if (ahead >= 2)
+      wait_vmcnt<2 * C::LPS>();
+    else if (ahead == 1)
+      wait_vmcnt<C::LPS>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (kt + S - 1 < nk) load_stage(kt + S - 1, std::integral_constant<int, (Bc + S - 1) % S>{});
+    compute(b);
+  };
+  // main loop: every step has S-2 later stages in flight and requests one more
+  auto step_full = [&](int kt, auto b) __attribute__((always_inline)) {
+    constexpr int Bc = decltype(b)::value;
+    wait_vmcnt<(S - 2) * C::LPS>();
+    lds_barrier();
+    load_stage(kt + S - 1, std::integral_constant<int, (Bc + S - 1) % S>{});
+    compute(b);
+  };
+  int kt = 0;
+  for (; kt + 2 * S - 2 < nk; kt += S) {
+    step_full(kt, B0{});
+    step_full(kt + 1, B1{});
+    if (S > 2) step_full(kt + 2, B2{});
+    if (S > 3) step_full(kt + 3, B3{});
+  }
+  // tail: at most 2 S - 2 stages, buffers continuing the rotation
+  for (int r = 0; r < 2 * S - 2 && kt < nk; ++r, ++kt) {
+    switch (kt % S) {
+      case 0: step(kt, B0{}); break;
+      case 1: step(kt, B1{}); break;
+      case 2: if (S > 2) step(kt, B2{}); break;
+      default: if (S > 3) step(kt, B3{}); break;
+    }
+  }
+
+  // ---- epilogue: D[n][m] holds, in lane (m = l32), rows n = 8 (r/4) + 4 hh + r%4:
+  // four consecutive n per register quad -> one 8-byte store each
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) {
+    const int m = m0 + wm * C::TM + j * 32 + l32;
+    if (m >= M) continue;
+    bf16* yrow = Y + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = n0 + wn * C::TN + i * 32 + 8 * r4 + 4 * hh;
+        if (n >= N) continue;
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[i][j][4 * r4 + 0], acc[i][j][4 * r4 + 1]);
+        v[1] = pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+        *(u32x2*)(yrow + n) = v;
+      }
+  }
+}
+
+// The kernels are plain (non-template) functions around the templated body: the host
+// pass then never instantiates device-only builtins.
+__global__ __launch_bounds__(512, 1) void gemm_lds_wide_kernel(GemmArgs p, int nb1, int nmb,
+                                                               int total) {
+  gemm_lds_body<256, 128, 3, 4, 2>(p, nb1, nmb, total);
+}
+__global__ __launch_bounds__(256, 2) void gemm_lds_narrow_kernel(GemmArgs p, int nb1, int nmb,
+                                                                 int total) {
+  gemm_lds_body<64, 64, 4, 2, 2>(p, nb1, nmb, total);
+}
+
+template <int BM, int BN, int NT>
+hipError_t launch_cfg(void (*kernel)(GemmArgs, int, int, int), const GemmArgs& p,
+                      hipStream_t s) {
+  const int nmb = (p.M + BM - 1) / BM;
+  const int nb1 = (p.N + BN - 1) / BN;
+  const int nb2 = p.w2 ? (p.N2 + BN - 1) / BN : 0;
+  const long total = (long)nmb * (nb1 + nb2);
+  if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(NT), 0, s, p, nb1, nmb, (int)total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_lds_supported(const GemmArgs& p) {
+  const auto al = [](const void* q, uintptr_t a) { return ((uintptr_t)q % a) == 0; };
+  if (p.g || p.K % BK || p.N % 8 || (p.w2 && p.N2 % 8)) return false;
+  if (!al(p.x, 16) || !al(p.w, 16) || !al(p.y, 8) || (p.w2 && (!al(p.w2, 16) || !al(p.y2, 8))))
+    return false;
+  // byte offsets inside one block's rows are 32-bit
+  return (int64_t)256 * p.K * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_lds(const GemmArgs& p, hipStream_t s) {
+  // Wide outputs: 256 x 128 tiles, 8 waves of 64 x 64, 3 stages (144 KB of LDS, one
+  // workgroup per CU).  Narrow outputs (too few such tiles to fill 256 CUs): 64 x 64
+  // tiles, 4 waves of 32 x 32, 4 stages (64 KB, two workgroups per CU).
+  const long big = (long)((p.M + 255) / 256) *
+                   ((p.N + 127) / 128 + (p.w2 ? (p.N2 + 127) / 128 : 0));
+  if (big >= 512) return launch_cfg<256, 128, 512>(gemm_lds_wide_kernel, p, s);
+  return launch_cfg<64, 64, 256>(gemm_lds_narrow_kernel, p, s);
+}
+
+}  // namespace gmla

@@ -95,6 +95,10 @@ struct GemmArgs {
   void* y2;        // [M, N2] or NULL
 };
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
+// LDS-direct pipelined bf16 GEMM: no gate, K a multiple of 64, N (and N2) a multiple
+// of 8, 16-byte aligned operands, 8-byte aligned outputs.
+bool gemm_lds_supported(const GemmArgs& a);
+hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gate_only(int dtype, int64_t n, const void* g, const void* x, void* y,
                             hipStream_t s);
 

@@ -197,6 +197,36 @@ def test_linear(M, N, K, dtype):
         check_rows_rel(host(y), ref, N)
 
 
+@pytest.mark.parametrize("M,N,K", [(2000, 8200, 320), (2048, 8192, 64), (1500, 11000, 192)])
+def test_linear_wide_ragged(M, N, K):
+    """Wide bf16 products (enough 256 x 128 tiles to take the multi-stage kernel): M and N
+    not multiples of the tile, K one stage or a few; sampled output rows."""
+    dev = need_gpu()
+    announce(f"linear wide {M}x{N}x{K}")
+    x = I.normal((M, K), torch.bfloat16, dev, seed=4300 + K)
+    w = I.normal((N, K), torch.bfloat16, dev, seed=4301 + K, std=K ** -0.5)
+    y = gm.linear(x, w)
+    torch.cuda.synchronize()
+    rows = sorted(set(list(range(0, M, 97)) + [M - 1, M - 2, 255, 256]))
+    ref = oracle.linear(host(x)[rows], host(w))
+    check_rows_rel(host(y)[rows], ref, N)
+
+
+def test_latent_expand_wide_ragged():
+    """Both outputs of one launch in the multi-stage kernel, widths not a tile multiple."""
+    dev = need_gpu()
+    announce("latent_expand wide 2000x4104x320")
+    M, dc, dm = 2000, 320, 4104
+    c = I.normal((M, dc), torch.bfloat16, dev, seed=4110)
+    wk = I.normal((dm, dc), torch.bfloat16, dev, seed=4111, std=dc ** -0.5)
+    wv = I.normal((dm, dc), torch.bfloat16, dev, seed=4112, std=dc ** -0.5)
+    K, V = gm.latent_expand(c, wk, wv)
+    torch.cuda.synchronize()
+    rows = sorted(set(list(range(0, M, 131)) + [M - 1, 1999 - 256]))
+    for got, w in ((K, wk), (V, wv)):
+        check_rows_rel(host(got)[rows], oracle.linear(host(c)[rows], host(w)), dm)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_latent_expand(dtype):
     dev = need_gpu()
