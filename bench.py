@@ -82,22 +82,25 @@ def measured_traffic(kernel: str):
 
 
 def time_calls(torch, fn, steps, warmup, rotate=1):
-    """Run fn(i) warmup + steps times; return per-call milliseconds of the timed calls
-    (HIP events on the current stream) and the wall time of the timed region."""
+    """Run fn(i) warmup + steps times back to back; return the average milliseconds per
+    call over the timed region (HIP events on the current stream before the first and
+    after the last timed call, so launch gaps count against the kernel), the fastest
+    single call (events between consecutive calls) and the wall time of the region."""
     for i in range(warmup):
         fn(i % rotate)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
+    evs[0].record(stream)
     for i in range(steps):
-        evs[i][0].record(stream)
         fn(i % rotate)
-        evs[i][1].record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return [a.elapsed_time(b) for a, b in evs], wall
+    region = evs[0].elapsed_time(evs[-1])
+    fastest = min(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    return region / steps, fastest, wall
 
 
 def cpu_prefill_baseline(q, k, v, budget_s=12.0):
@@ -313,8 +316,7 @@ def main():
         q, k, v, _ = I.workload_inputs(pw.name, dev)
         out = torch.empty((d["B"], d["T"], d["H"] * d["D"]), dtype=q.dtype, device=dev)
         flops = prefill_flops(d["B"], d["T"], d["H"], d["D"])
-        ms, wall = time_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), K, W)
-        avg = sum(ms) / len(ms)
+        avg, fastest, wall = time_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), K, W)
         tflops = flops / (avg * 1e-3) / 1e12
         result.update({
             "value": round(tflops, 2), "ms_per_step": round(wall * 1e3 / K, 4),
@@ -324,7 +326,7 @@ def main():
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_bf16_kernel"),
                          "kernel": "prefill_bf16_kernel", "algorithmic_flop_per_launch": flops,
-                         "avg_launch_ms": round(avg, 4), "min_launch_ms": round(min(ms), 4)},
+                         "avg_launch_ms": round(avg, 4), "min_launch_ms": round(fastest, 4)},
         })
 
     # ---------------- decode: B=8 H=96 N=1001 D=128 bf16, rotated over 4 input sets
@@ -347,12 +349,12 @@ def main():
             qd, kd, vd, od = sets[i]
             gm.attend_decode(qd, kd, vd, num_splits=splits, workspace=ws, out=od)
 
-        dms, dwall = time_calls(torch, dec, max(K, 20), W, rotate=4)
-        davg = sum(dms) / len(dms)
+        dcalls = max(K, 20)
+        davg, dfast, dwall = time_calls(torch, dec, dcalls, W, rotate=4)
         gbps = nbytes / (davg * 1e-3) / 1e9
         result["decode"] = {
             "workload": dw.name, "value": round(gbps, 1), "unit": "GB/s", "splits": splits,
-            "calls": len(dms), "avg_call_ms": round(davg, 5), "min_call_ms": round(min(dms), 5),
+            "calls": dcalls, "avg_call_ms": round(davg, 5), "min_call_ms": round(dfast, 5),
             "rotation": "4 input sets (1.58 GB) cycled so the 256 MB last-level cache cannot hold them",
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
@@ -362,7 +364,7 @@ def main():
         }
         if only == "decode":
             result.update({"value": round(gbps, 1), "unit": "GB/s",
-                           "ms_per_step": round(dwall * 1e3 / len(dms), 4)})
+                           "ms_per_step": round(dwall * 1e3 / dcalls, 4)})
 
     if args.all or only in ("layer", "decode_long"):
         extra = {}
@@ -370,13 +372,12 @@ def main():
             lw = I.WORKLOADS["layer_t2048"]
             ld = lw.dims
             x, wts = I.workload_inputs(lw.name, dev)
-            lms, _ = time_calls(torch, lambda i: gm.gated_mla(x, wts["Wq"], wts["Wc"], wts["Wk"],
+            lavg, _, _ = time_calls(torch, lambda i: gm.gated_mla(x, wts["Wq"], wts["Wc"], wts["Wk"],
                                                               wts["Wv"], wts["Wg"], wts["Wo"],
                                                               ld["H"], True),
                                 max(5, K // 5), 2)
             T_, dm, dc = ld["T"], ld["d_model"], ld["d_c"]
             lflops = 2 * T_ * (3 * dm * dm + 3 * dm * dc) + prefill_flops(1, T_, ld["H"], dm // ld["H"])
-            lavg = sum(lms) / len(lms)
             extra[lw.name] = {"value": round(lflops / (lavg * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
                               "avg_call_ms": round(lavg, 4), "algorithmic_flop": lflops}
             del x, wts
@@ -384,8 +385,7 @@ def main():
             cw = I.WORKLOADS["decode_b4_n131072"]
             cd = cw.dims
             qc, kc, vc, _ = I.workload_inputs(cw.name, dev)
-            cms, _ = time_calls(torch, lambda i: gm.attend_decode(qc, kc, vc), max(5, K // 5), 2)
-            cavg = sum(cms) / len(cms)
+            cavg, _, _ = time_calls(torch, lambda i: gm.attend_decode(qc, kc, vc), max(5, K // 5), 2)
             cb = decode_bytes(cd["B"], cd["H"], cd["N"], cd["D"])
             extra[cw.name] = {"value": round(cb / (cavg * 1e-3) / 1e9, 1), "unit": "GB/s",
                               "avg_call_ms": round(cavg, 4), "algorithmic_bytes": cb,

@@ -182,22 +182,30 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
 
+  // One stage: 4 k-steps of 16; the fragments of k-step ks+1 are requested before the
+  // MFMAs of k-step ks, so their LDS latency is covered (the fences keep that order).
   auto compute = [&](auto b) __attribute__((always_inline)) {
     const char* xt = (const char*)xbuf(b) + wm * C::TM * 128;
     const char* wt = (const char*)wbuf(b) + wn * C::TN * 128;
     const int fl = opaque(frag_lane);
+    bf16x8 xf[2][C::FM], wf[2][C::FN];
+    auto rd = [&](int ks, int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) xf[slot][j] = *(const bf16x8*)(xt + j * 4096 + (fl ^ (ks << 5)));
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) wf[slot][i] = *(const bf16x8*)(wt + i * 4096 + (fl ^ (ks << 5)));
+    };
+    rd(0, 0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 xf[C::FM], wf[C::FN];
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j) xf[j] = *(const bf16x8*)(xt + j * 4096 + (fl ^ (ks << 5)));
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i) wf[i] = *(const bf16x8*)(wt + i * 4096 + (fl ^ (ks << 5)));
+      if (ks + 1 < BK / 16) rd(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
         for (int j = 0; j < C::FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][i], xf[ks & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
