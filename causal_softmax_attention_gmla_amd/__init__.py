@@ -6,6 +6,7 @@ that tensor shapes agree with the sizes they pass, allocate outputs with PyTorch
 the library; every arithmetic step runs in the library's HIP kernels.
 
     attend_prefill(q, k, v, gate=None, scale=None, causal=True)   -> [B, T, H*D]
+    attend_chunk(q, k, v, gate=None, scale=None, causal=True)     -> [B, Tq, H*D]
     attend_decode(q, k, v, gate=None, scale=None, num_splits=0)   -> [B, H*D]
     latent_expand(c, w_k, w_v)                                    -> (K, V)
     gate_out(o_tilde, w_o=None, gate=None)                        -> Y
@@ -27,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import GMLA_BF16, GMLA_F32, GmlaError, LIB_PATH  # noqa: F401
 
-__all__ = ["attend_prefill", "attend_decode", "latent_expand", "gate_out", "linear", "gated_mla",
+__all__ = ["attend_prefill", "attend_chunk", "attend_decode", "latent_expand", "gate_out", "linear", "gated_mla",
            "decode_num_splits", "decode_workspace_bytes", "library", "GmlaError"]
 
 _DTYPES = {torch.float32: GMLA_F32, torch.bfloat16: GMLA_BF16}
@@ -111,6 +112,47 @@ def attend_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torc
                                          _ptr(q), _ptr(k), _ptr(v), strides, _ptr(gate), _ptr(out),
                                          _stream(dev, stream))
     _lib.check(st, "gmla_attend_prefill")
+    return out
+
+
+def attend_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor | None = None,
+                 *, scale: float | None = None, causal: bool = True, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Attention of Tq new queries that follow Tk - Tq cached tokens: query i sits at
+    position i + Tk - Tq and (causal) sees keys 0..i + Tk - Tq.
+
+    q: [B, Tq, H, D]; k, v: [B, Tk, H, D] (the cache followed by the chunk) with
+    identical strides; every last axis contiguous.  gate: optional [B, Tq, H*D] logits.
+    Returns [B, Tq, H*D].
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, Tq, H, D] and k, v [B, Tk, H, D]")
+    B, Tq, H, D = q.shape
+    Tk = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (B, H, D):
+        raise ValueError("q and k, v disagree in batch, heads or head width")
+    if Tk < Tq:
+        raise ValueError("the chunk cannot be longer than the key sequence")
+    if k.stride() != v.stride() or k.stride(3) != 1 or q.stride(3) != 1:
+        raise ValueError("k, v need identical strides; every last axis must be contiguous")
+    if not isinstance(causal, bool):
+        raise TypeError("causal must be a bool")
+    dev = _dev(q, k, v, gate, out)
+    _same_dtype(q, k, v, gate, out)
+    if gate is not None and (gate.shape != (B, Tq, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [B, Tq, H*D] tensor")
+    if out is None:
+        out = torch.empty((B, Tq, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (B, Tq, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Tq, H*D] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qs = (ctypes.c_int64 * 3)(q.stride(0), q.stride(1), q.stride(2))
+    kvs = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    st = _lib.load().gmla_attend_chunk(_dtype(q), B, Tq, Tk, H, D, float(scale), int(causal),
+                                       _ptr(q), qs, _ptr(k), _ptr(v), kvs, _ptr(gate), _ptr(out),
+                                       _stream(dev, stream))
+    _lib.check(st, "gmla_attend_chunk")
     return out
 
 

@@ -27,6 +27,8 @@ SIGNATURES = {
     "gmla_status_string": (ctypes.c_char_p, [_i]),
     "gmla_version": (_i, []),
     "gmla_attend_prefill": (_i, [_i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _i64p, _vp, _vp, _vp]),
+    "gmla_attend_chunk": (_i, [_i, _i, _i, _i, _i, _i, _f, _i, _vp, _i64p, _vp, _vp, _i64p, _vp,
+                               _vp, _vp]),
     "gmla_decode_num_splits": (_i, [_i, _i, _i, _i]),
     "gmla_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "gmla_attend_decode": (_i, [_i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _i64p, _vp, _vp, _vp,

@@ -44,25 +44,40 @@ const char* gmla_status_string(int status) {
 
 int gmla_version(void) { return kVersion; }
 
-int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int causal,
-                        const void* Q, const void* K, const void* V, const int64_t* strides,
-                        const void* G, void* O, void* stream) {
-  if (!valid_dtype(dtype) || B <= 0 || T <= 0 || H <= 0 || D <= 0) return GMLA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Shared by the square prefill and the chunk entry points: Tq query rows against Tk >= Tq
+// key rows, query i at position i + Tk - Tq.
+int attend_impl(int dtype, int B, int Tq, int Tk, int H, int D, float scale, int causal,
+                const void* Q, const int64_t* q_strides, const void* K, const void* V,
+                const int64_t* kv_strides, const void* G, void* O, void* stream) {
+  if (!valid_dtype(dtype) || B <= 0 || Tq <= 0 || Tk < Tq || H <= 0 || D <= 0)
+    return GMLA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return GMLA_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O) return GMLA_ERR_INVALID_ARG;
   if (!(scale == scale) || scale <= 0.0f) return GMLA_ERR_INVALID_ARG;
   PrefillArgs a;
-  a.B = B; a.T = T; a.H = H; a.D = D;
+  a.B = B; a.T = Tq; a.Tk = Tk; a.H = H; a.D = D;
   a.scale = scale;
   a.causal = causal;
   a.q = Q; a.k = K; a.v = V; a.g = G; a.o = O;
-  if (strides) {
-    a.sb = strides[0]; a.st = strides[1]; a.sh = strides[2];
+  if (q_strides) {
+    a.qsb = q_strides[0]; a.qst = q_strides[1]; a.qsh = q_strides[2];
+    if (a.qsb < 0 || a.qst < 0 || a.qsh < 0) return GMLA_ERR_INVALID_ARG;
+  } else {
+    a.qsh = D;
+    a.qst = (int64_t)H * D;
+    a.qsb = (int64_t)Tq * H * D;
+  }
+  if (kv_strides) {
+    a.sb = kv_strides[0]; a.st = kv_strides[1]; a.sh = kv_strides[2];
     if (a.sb < 0 || a.st < 0 || a.sh < 0) return GMLA_ERR_INVALID_ARG;
   } else {
     a.sh = D;
     a.st = (int64_t)H * D;
-    a.sb = (int64_t)T * H * D;
+    a.sb = (int64_t)Tk * H * D;
   }
   const size_t es = elem_size(dtype);
   if (!aligned(Q, es) || !aligned(K, es) || !aligned(V, es) || !aligned(O, es) ||
@@ -74,13 +89,14 @@ int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int 
   if (dtype == GMLA_BF16 && D == 128) {
     // 16-byte fragment loads: every row start must be 16-byte aligned
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
-        (G && !aligned(G, 16)) || a.sb % 8 || a.st % 8 || a.sh % 8)
+        (G && !aligned(G, 16)) || a.sb % 8 || a.st % 8 || a.sh % 8 || a.qsb % 8 || a.qst % 8 ||
+        a.qsh % 8)
       return GMLA_ERR_INVALID_ARG;
-    // byte offsets inside one 64-token tile are 32-bit
+    // byte offsets inside one 64-token key tile are 32-bit
     if (a.st >= (int64_t)1 << 24) return GMLA_ERR_UNSUPPORTED;
     if (log_enabled())
-      fprintf(stderr, "gmla: prefill bf16 mfma B=%d T=%d H=%d causal=%d gate=%d\n", B, T, H,
-              causal, G != nullptr);
+      fprintf(stderr, "gmla: prefill bf16 mfma B=%d Tq=%d Tk=%d H=%d causal=%d gate=%d\n", B, Tq,
+              Tk, H, causal, G != nullptr);
     e = launch_prefill_bf16_mfma(a, s);
   } else if (dtype == GMLA_BF16) {
     e = launch_prefill_simple_bf16(a, s);
@@ -88,6 +104,23 @@ int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int 
     e = launch_prefill_simple_f32(a, s);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int causal,
+                        const void* Q, const void* K, const void* V, const int64_t* strides,
+                        const void* G, void* O, void* stream) {
+  return attend_impl(dtype, B, T, T, H, D, scale, causal, Q, strides, K, V, strides, G, O, stream);
+}
+
+int gmla_attend_chunk(int dtype, int B, int Tq, int Tk, int H, int D, float scale, int causal,
+                      const void* Q, const int64_t* q_strides, const void* K, const void* V,
+                      const int64_t* kv_strides, const void* G, void* O, void* stream) {
+  return attend_impl(dtype, B, Tq, Tk, H, D, scale, causal, Q, q_strides, K, V, kv_strides, G, O,
+                     stream);
 }
 
 int gmla_decode_num_splits(int B, int H, int N, int D) {

@@ -60,13 +60,15 @@ template <> struct Elem<bf16> {
 // Each returns a hipError_t from the launch; arguments are already validated.
 
 struct PrefillArgs {
-  int B, T, H, D;
+  int B, T, H, D;         // T: query rows
+  int Tk;                 // key rows (>= T); query i sits at position i + Tk - T
   float scale;
   int causal;
   const void *q, *k, *v;
-  int64_t sb, st, sh;  // element strides of Q, K, V (batch, token, head); d is contiguous
-  const void* g;       // nullable gate logits [B, T, H*D]
-  void* o;             // [B, T, H*D]
+  int64_t qsb, qst, qsh;  // element strides of Q (batch, token, head); d is contiguous
+  int64_t sb, st, sh;     // element strides of K and V (batch, token, head)
+  const void* g;          // nullable gate logits [B, T, H*D]
+  void* o;                // [B, T, H*D]
 };
 hipError_t launch_prefill_bf16_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_simple_f32(const PrefillArgs& a, hipStream_t s);

@@ -35,7 +35,10 @@
 //    which skips most O rescales; the stale maximum scales numerator and
 //    denominator alike, so the result is unchanged.
 //  * Causal tiles above the diagonal are never loaded; the mask is an index compare
-//    applied only on the two tiles that straddle the diagonal or the sequence end.
+//    applied only on the tiles that straddle the diagonal or the sequence end.
+//  * The queries may be the last T rows of Tk >= T keys (a chunk after a cache):
+//    query i sits at position i + Tk - T and sees the keys up to there ("Kimi K2 -
+//    Construct causal mask": positions continue from the cached length).
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
 //    (shared L2), heaviest (longest-prefix) blocks first.
 #include <type_traits>
@@ -81,11 +84,11 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Buffer resource over rows [tile*BN, tile*BN + BN) of one head; rows at or past T
-// (and whole tiles past the end) fall outside its range and load as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* head, int tile, int T,
+// Buffer resource over rows [tile*BN, tile*BN + BN) of one head; key rows at or past
+// Tk (and whole tiles past the end) fall outside its range and load as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const bf16* head, int tile, int Tk,
                                                            int64_t st) {
-  const int rows = min(BN, T - tile * BN);
+  const int rows = min(BN, Tk - tile * BN);
   const int bytes = rows > 0 ? (int)(((int64_t)(rows - 1) * st + HD) * 2) : 0;
   return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (int64_t)tile * BN * st), (short)0, bytes,
                                            kBufferDword3);
@@ -109,7 +112,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int b = head_lin / a.H;
   const int h = head_lin % a.H;
   const int q0 = qb * BM;
-  const int T = a.T;
+  const int T = a.T;             // query rows
+  const int Tk = a.Tk;           // key rows
+  const int off = a.Tk - a.T;    // position of query 0
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int hh = lane >> 5;
 
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const bf16* __restrict__ Qh = (const bf16*)a.q + head_off;
+  const bf16* __restrict__ Qh = (const bf16*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
   const bf16* __restrict__ Kh = (const bf16*)a.k + head_off;
   const bf16* __restrict__ Vh = (const bf16*)a.v + head_off;
   const int64_t st = a.st;
@@ -130,16 +135,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     if (tq < T)
-      qf[ks] = *(const bf16x8*)(Qh + (int64_t)tq * st + ks * 16 + hh * 8);
+      qf[ks] = *(const bf16x8*)(Qh + (int64_t)tq * a.qst + ks * 16 + hh * 8);
     else
       qf[ks] = bf16x8{};
   }
 
   // ---- key tiles this workgroup visits
-  const int nkt_all = (T + BN - 1) / BN;
-  const int ntiles = a.causal ? min(nkt_all, (q0 + BM) / BN) : nkt_all;
-  // first tile that needs the index mask: the diagonal pair (causal) or the tail
-  const int mask_from = a.causal ? ntiles - 2 : (T % BN ? ntiles - 1 : ntiles);
+  const int nkt_all = (Tk + BN - 1) / BN;
+  const int ntiles = a.causal ? min(nkt_all, (q0 + BM - 1 + off) / BN + 1) : nkt_all;
+  // first tile that needs the index mask: the one holding the key just after the
+  // block's first query (causal; the diagonal band and the tail follow it), or the
+  // ragged tail (non-causal)
+  const int mask_from =
+      a.causal ? min(ntiles, (q0 + off + 1) / BN) : (Tk % BN ? ntiles - 1 : ntiles);
 
   // Tile staging: each wave moves 4 KB of a tile (4 loads of 64 lanes x 16 bytes).
   // Load u of wave w fills LDS rows 4m .. 4m+3 (m = 4w + u) in physical chunk order;
@@ -152,13 +160,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     voff[u] = (uint32_t)((row * st + v_chunk(row, lane & 15) * 8) * 2);
   }
   auto load_k = [&](int tile, auto buf) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kh, tile, T, st);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Kh, tile, Tk, st);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       load_lds16(r, k_buf<decltype(buf)::value>() + (wave * 4 + u) * 512, koff[u]);
   };
   auto load_v = [&](int tile, auto buf) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vh, tile, T, st);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(Vh, tile, Tk, st);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       load_lds16(r, v_buf<decltype(buf)::value>() + (wave * 4 + u) * 512, voff[u]);
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   bf16x2 ones2;
   ones2[0] = (bf16)1.0f;
   ones2[1] = (bf16)1.0f;
-  const int lim = a.causal ? min(tq, T - 1) : T - 1;  // last key this query may see
+  const int lim = a.causal ? min(tq + off, Tk - 1) : Tk - 1;  // last key this query may see
 
   // keys after the query (causal) or past the sequence end score -inf
   auto mask = [&](f32x16* s, int tile) __attribute__((always_inline)) {

@@ -6,6 +6,10 @@
 // with the optional channel-wise sigmoid gate ("Gated MLA", section "The
 // channel-wise output gate").
 //
+// Queries may be the last rows of a longer key sequence (a chunk after a cache): query
+// i then sits at position i + Tk - T ("Kimi K2 - Construct causal mask": positions
+// continue from the cached length).
+//
 // One 64-lane workgroup takes 64 / TPQ queries of one (batch, head); each query is
 // owned by TPQ lanes that split its head channels (DP channels each).  Key and value
 // tiles of 64 rows are staged in LDS as float32; every lane keeps its query slice,
@@ -35,29 +39,30 @@ __global__ __launch_bounds__(64) void prefill_simple_kernel(PrefillArgs a) {
   const int qi = tid % QPB;   // query slot in the workgroup
   const int part = tid / QPB;  // channel slice
   const int t = qb * QPB + qi;
-  const int T = a.T;
+  const int T = a.T, Tk = a.Tk, off = a.Tk - a.T;
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const E* Qh = (const E*)a.q + head_off;
+  const E* Qh = (const E*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
   const E* Kh = (const E*)a.k + head_off;
   const E* Vh = (const E*)a.v + head_off;
 
   float q[DP], o[DP];
 #pragma unroll
   for (int i = 0; i < DP; ++i) {
-    q[i] = t < T ? Elem<E>::load(Qh + (int64_t)t * a.st + part * DP + i) : 0.0f;
+    q[i] = t < T ? Elem<E>::load(Qh + (int64_t)t * a.qst + part * DP + i) : 0.0f;
     o[i] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
-  const int last_visible = a.causal ? min(t, T - 1) : T - 1;
-  const int block_last = a.causal ? min(qb * QPB + QPB - 1, T - 1) : T - 1;
+  // query t sits at position t + off: it sees keys up to there (causal) or all of them
+  const int last_visible = a.causal ? min(t + off, Tk - 1) : Tk - 1;
+  const int block_last = a.causal ? min(qb * QPB + QPB - 1 + off, Tk - 1) : Tk - 1;
 
   for (int k0 = 0; k0 <= block_last; k0 += KT) {
     __syncthreads();
     for (int idx = tid; idx < KT * D; idx += 64) {
       const int r = idx / D, c = idx % D;
       const int key = k0 + r;
-      ks[r][c] = key < T ? Elem<E>::load(Kh + (int64_t)key * a.st + c) : 0.0f;
-      vs[r][c] = key < T ? Elem<E>::load(Vh + (int64_t)key * a.st + c) : 0.0f;
+      ks[r][c] = key < Tk ? Elem<E>::load(Kh + (int64_t)key * a.st + c) : 0.0f;
+      vs[r][c] = key < Tk ? Elem<E>::load(Vh + (int64_t)key * a.st + c) : 0.0f;
     }
     __syncthreads();
     // scores of this tile; keys after the query (or past the end) get -inf

@@ -82,6 +82,26 @@ int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int 
                         const void* G, void* O, void* stream);
 
 /*
+ * Attention of a chunk of Tq queries that follow Tk - Tq cached tokens (chunked
+ * prefill, several new tokens at once): query i of the chunk sits at absolute
+ * position p_i = i + Tk - Tq, positions continuing from the cached length ("Kimi K2 -
+ * Construct causal mask"; "Kimi K3 - Softmax over keys", decode at position 1000 with
+ * 1001 keys), and with causal = 1 it sees the keys s <= p_i (bottom-right aligned);
+ * with causal = 0 it sees all Tk keys.  Same formula, gate and supported types as
+ * gmla_attend_prefill, which is this call with Tq = Tk and one set of strides.
+ *
+ *   Q : element (b, i, h, d) at b*q_strides[0] + i*q_strides[1] + h*q_strides[2] + d
+ *       (NULL: contiguous [B, Tq, H, D]).
+ *   K,V: element (b, s, h, d) at b*kv_strides[0] + s*kv_strides[1] + h*kv_strides[2] + d
+ *       (NULL: contiguous [B, Tk, H, D]), s < Tk: the cache followed by the chunk.
+ *   G : nullable, contiguous [B, Tq, H*D];  O : contiguous [B, Tq, H*D].
+ * Requires 1 <= Tq <= Tk (else GMLA_ERR_INVALID_ARG).
+ */
+int gmla_attend_chunk(int dtype, int B, int Tq, int Tk, int H, int D, float scale, int causal,
+                      const void* Q, const int64_t* q_strides, const void* K, const void* V,
+                      const int64_t* kv_strides, const void* G, void* O, void* stream);
+
+/*
  * Decode: one new query per (b, h) against N cached keys.  The query sits at
  * position N - 1, so every cached key is visible ("Kimi K3 - Softmax over keys":
  * the query at p = 1000 reads 1001 keys).  The keys are split into num_splits

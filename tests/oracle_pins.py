@@ -195,6 +195,32 @@ def pin_decode_alignment(orc):
     assert A2[0, -1] == 0.0 and np.all(A2[0, :-1] > 0) and np.all(A2[1] > 0)
 
 
+def pin_chunk_alignment(orc):
+    """Kimi K2 - Construct causal mask: positions continue from the cached length, so
+    a chunk of Tq queries after Tk - Tq cached tokens puts query i at position
+    i + Tk - Tq.  With Q = 0 the weights are uniform over the visible keys, so row i is
+    the mean of V rows 0 .. i + Tk - Tq (a closed form that fixes the alignment); the
+    chunk's rows are the last Tq rows of the square causal attention over all Tk
+    tokens; without the mask every query sees all Tk keys."""
+    r = _rng(12)
+    Tk, Tq, D = 70, 23, 8
+    off = Tk - Tq
+    k, v = r.standard_normal((Tk, D)), r.standard_normal((Tk, D))
+    out = orc.attend_head(np.zeros((Tq, D)), k, v, 0.5, True)
+    counts = np.arange(off + 1, Tk + 1)
+    ref = np.cumsum(v, axis=0)[off:] / counts[:, None]
+    assert np.max(np.abs(out - ref)) <= 1e-13
+    q_full = r.standard_normal((Tk, D))
+    chunk = orc.attend_head(q_full[off:], k, v, 0.5, True)
+    square = orc.attend_head(q_full, k, v, 0.5, True)
+    assert np.max(np.abs(chunk - square[off:])) <= 1e-14
+    _, A = orc.attend_head(q_full[off:], k, v, 0.5, False, want_probs=True)
+    assert np.all(A > 0.0)
+    _, A = orc.attend_head(q_full[off:], k, v, 0.5, True, want_probs=True)
+    for i in range(Tq):
+        assert np.all(A[i, : off + i + 1] > 0.0) and np.all(A[i, off + i + 1:] == 0.0)
+
+
 def pin_scaled_score_variance(orc):
     """Le Transformer et l'attention, 'Vérification de compréhension': with unit
     variance q and k, q.k / sqrt(d_k) has variance 1.  The spread of the log-weights

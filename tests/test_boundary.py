@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import causal_softmax_attention_gmla_amd as gm
 from causal_softmax_attention_gmla_amd import _lib
@@ -68,6 +69,31 @@ def test_prefill_rejects_misaligned_strides():
     assert _prefill(strides=s) == -1
     neg = (ctypes.c_int64 * 3)(-1, 256, 128)
     assert _prefill(strides=neg) == -1
+
+
+def _chunk(**kw):
+    a = dict(dtype=1, B=1, Tq=8, Tk=40, H=2, D=128, scale=0.1, causal=1, Q=FAKE, q_strides=None,
+             K=FAKE, V=FAKE, kv_strides=None, G=None, O=FAKE, stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_chunk(*a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(Tq=0), dict(Tq=41), dict(Tk=0), dict(B=0), dict(causal=2),
+                                 dict(Q=None), dict(K=None), dict(scale=0.0),
+                                 dict(q_strides=(ctypes.c_int64 * 3)(-8, 256, 128)),
+                                 dict(kv_strides=(ctypes.c_int64 * 3)(40 * 256, 256 + 4, 128))])
+def test_chunk_rejects_bad_arguments(bad):
+    """A chunk needs 1 <= Tq <= Tk, valid strides (multiples of 8 for the MFMA path)."""
+    assert _chunk(**bad) == -1
+
+
+def test_chunk_wrapper_checks_shapes():
+    q = torch.zeros((1, 9, 2, 128), dtype=torch.bfloat16)
+    k = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gm.attend_chunk(q, k, k)  # chunk longer than the key sequence
+    with pytest.raises(ValueError):
+        gm.attend_chunk(q[:, :4], k[:, :, :1], k[:, :, :1])  # head count differs
 
 
 def _decode(**kw):

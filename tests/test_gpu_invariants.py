@@ -61,6 +61,24 @@ def test_future_keys_do_not_change_past_rows_bitwise():
     assert not torch.equal(a[:, t0 + 1:], b[:, t0 + 1:])
 
 
+@pytest.mark.parametrize("off", [0, 64, 100, 191])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_chunk_rows_equal_full_prefill_rows(off, dtype, D):
+    """Positions continue from the cached length ('Kimi K2 - Construct causal mask'): the
+    attention of the last T - off queries as a chunk over all T keys is, row for row,
+    the causal prefill of the whole sequence.  Each row sees the same keys in the same
+    tile order, and the extra tiles a chunk block may visit are fully masked for its
+    rows (zero weights), so the rows agree bitwise."""
+    dev = need_gpu()
+    announce(f"invariant chunk == prefill rows off={off} {dtype}")
+    B, T, H = 2, 333, 2
+    q, k, v, g = I.prefill_inputs(B, T, H, D, dtype, dev, seed=6300 + off, gate=True)
+    full = gm.attend_prefill(q, k, v, g)
+    part = gm.attend_chunk(q[:, off:], k, v, g[:, off:].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(full[:, off:], part)
+
+
 @pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 32)])
 def test_first_row_is_first_value_bitwise(dtype, D):
     """Query 0 sees only key 0: its weight is exactly 1 and the output is V[0]."""

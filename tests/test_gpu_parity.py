@@ -61,6 +61,43 @@ def test_prefill_bf16_mfma_shapes(T, causal):
     check_rows_rel(host(out), _oracle_prefill(q, k, v, g, causal), 128)
 
 
+# ---------------------------------------------------------------- chunk after a cache
+
+
+def _chunk_inputs(B, Tq, Tk, H, D, dtype, dev, seed, gate):
+    """Chunk queries [B, Tq, H, D] (contiguous) and keys/values [B, Tk, H, D] as head
+    views into one packed [B, Tk, 2, H, D] cache (strides differ from the queries')."""
+    q = I.normal((B, Tq, H, D), dtype, dev, seed)
+    kv = I.normal((B, Tk, 2, H, D), dtype, dev, seed + 1)
+    g = I.normal((B, Tq, H * D), dtype, dev, seed + 2) if gate else None
+    return q, kv[:, :, 0], kv[:, :, 1], g
+
+
+@pytest.mark.parametrize("Tq,Tk", [(1, 1001), (1, 64), (37, 300), (128, 256), (200, 777), (64, 64),
+                                   (129, 130), (300, 1000)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_bf16_mfma(Tq, Tk, causal):
+    """A chunk of Tq queries after Tk - Tq cached tokens (query i at position
+    i + Tk - Tq), offsets on and off the 64-key tile grid, on the MFMA kernel."""
+    dev = need_gpu()
+    announce(f"chunk bf16 D=128 Tq={Tq} Tk={Tk} causal={causal}")
+    q, k, v, g = _chunk_inputs(2, Tq, Tk, 3, 128, torch.bfloat16, dev, 2600 + Tq + Tk, Tq % 2 == 1)
+    out = gm.attend_chunk(q, k, v, g, causal=causal)
+    torch.cuda.synchronize()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, g, causal), 128)
+
+
+@pytest.mark.parametrize("Tq,Tk,D", [(5, 77, 32), (70, 133, 64), (33, 200, 128)])
+def test_chunk_f32_exact(Tq, Tk, D):
+    """The float32 kernel with an offset, to the float32 tolerance."""
+    dev = need_gpu()
+    announce(f"chunk f32 D={D} Tq={Tq} Tk={Tk}")
+    q, k, v, g = _chunk_inputs(1, Tq, Tk, 2, D, torch.float32, dev, 2700 + D, True)
+    out = gm.attend_chunk(q, k, v, g, causal=True)
+    torch.cuda.synchronize()
+    check_f32_abs(host(out), _oracle_prefill(q, k, v, g, True))
+
+
 @pytest.mark.parametrize("D", [32, 64])
 def test_prefill_bf16_small_heads(D):
     dev = need_gpu()
