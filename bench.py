@@ -103,6 +103,43 @@ def time_calls(torch, fn, steps, warmup, rotate=1):
     return region / steps, fastest, wall
 
 
+def measure_achievable(torch, dev):
+    """What the device reaches on this run: a register-only MFMA loop (bf16, two waves
+    per SIMD) and a plain non-temporal streaming read of 2 GiB (libgmla_probe.so)."""
+    import ctypes
+
+    path = os.path.join(HERE, "causal_softmax_attention_gmla_amd", "libgmla_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.gmla_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.gmla_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    blocks, iters = 512, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    flops = blocks * 4 * iters * 16 * 32 * 32 * 16 * 2
+
+    def mfma(i):
+        assert lib.gmla_probe_mfma(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp) == 0
+
+    mavg, _, _ = time_calls(torch, mfma, 5, 2)
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rblocks = 2048
+    rout = torch.empty(rblocks, dtype=torch.int32, device=dev)
+
+    def read(i):
+        assert lib.gmla_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks,
+                                   ctypes.c_void_p(rout.data_ptr()), sp) == 0
+
+    ravg, _, _ = time_calls(torch, read, 5, 2)
+    del buf
+    return {"mfma_bf16_tflops": round(flops / (mavg * 1e-3) / 1e12, 1),
+            "hbm_read_gbps": round(nbytes / (ravg * 1e-3) / 1e9, 1),
+            "how": "libgmla_probe.so: register-only v_mfma_f32_32x32x16_bf16 loop (512 x 256 "
+                   "threads, 4 chains per wave); 2 GiB non-temporal 16-byte read stream"}
+
+
 def cpu_prefill_baseline(q, k, v, budget_s=12.0):
     """The oracle on whole heads of the prefill workload until ~budget_s of CPU time."""
     import numpy as np
@@ -397,6 +434,18 @@ def main():
         result["cpu_baseline"] = cpu_prefill_baseline(q, k, v)
         qd, kd, vd, _ = sets[0]
         result["decode"]["cpu_baseline"] = cpu_decode_baseline(qd, kd, vd)
+
+    if only in (None, "prefill", "decode"):
+        ach = measure_achievable(torch, dev)
+        if "roofline" in result:
+            result["roofline"]["achievable"] = ach["mfma_bf16_tflops"]
+            result["roofline"]["frac_of_achievable"] = round(
+                result["roofline"]["achieved"] / ach["mfma_bf16_tflops"], 4)
+        if "decode" in result:
+            rl = result["decode"]["roofline"]
+            rl["achievable"] = ach["hbm_read_gbps"]
+            rl["frac_of_achievable"] = round(rl["achieved"] / ach["hbm_read_gbps"], 4)
+        result["achievable"] = ach
 
     print(json.dumps(result), flush=True)
 

@@ -18,9 +18,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgmla.so")
+PROBE_LIB = os.path.join(HERE, "libgmla_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["gmla_api.hip", "prefill_bf16.hip", "prefill_simple.hip", "decode.hip", "gemm.hip", "gemm_lds.hip"]
+# measurement aids for the benchmark, linked into their own library
+PROBE_SOURCES = ["probe.hip"]
 
 # -packed-fp32-ops: never emit packed float32 VALU instructions (v_pk_fma_f32 and
 # friends); the host pass prints a harmless "not a recognized feature" warning.
@@ -47,15 +50,7 @@ def _compile(src: str, obj: str, extra: list[str]) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(out: str = LIB, extra: list[str] | None = None, jobs: int = 8) -> str:
-    extra = list(extra or [])
-    objdir = os.path.join(HERE, "_build")
-    os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        futs = [ex.submit(_compile, s, o, extra) for s, o in zip(SOURCES, objs)]
-        for f in futs:
-            f.result()
+def _link(objs: list[str], out: str) -> str:
     tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
            "-Wl,-rpath,/opt/rocm/lib"]
@@ -63,6 +58,24 @@ def build(out: str = LIB, extra: list[str] | None = None, jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out)
+    return out
+
+
+def build(out: str = LIB, extra: list[str] | None = None, jobs: int = 8,
+          probe_out: str | None = PROBE_LIB) -> str:
+    """Compile and link libgmla.so (and, unless probe_out is None, libgmla_probe.so)."""
+    extra = list(extra or [])
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = SOURCES + (PROBE_SOURCES if probe_out else [])
+    objs = {s: os.path.join(objdir, s.replace(".hip", ".o")) for s in srcs}
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
+        futs = [ex.submit(_compile, s, objs[s], extra) for s in srcs]
+        for f in futs:
+            f.result()
+    _link([objs[s] for s in SOURCES], out)
+    if probe_out:
+        _link([objs[s] for s in PROBE_SOURCES], probe_out)
     return out
 
 

@@ -1,0 +1,72 @@
+// Measurement aids (libgmla_probe.so): a register-only matrix-core loop and a plain
+// streaming read, so the benchmark can report what the hardware reaches beside the
+// data-sheet peaks.  Nothing of the attention method is computed here.
+#include "../../include/gmla_probe.h"
+
+#include "gmla_internal.h"
+
+using namespace gmla;
+
+namespace {
+
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* out) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (bf16)(threadIdx.x * 0.001f + i);
+    b[i] = (bf16)0.5f;
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  }
+  float s = 0.0f;
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ p, size_t n,
+                                                         unsigned magic, unsigned* out) {
+  u32x4 acc = {0, 0, 0, 0};
+  const size_t stride = (size_t)gridDim.x * 256 * kReadUnroll;
+  for (size_t i = (size_t)blockIdx.x * 256 * kReadUnroll + threadIdx.x;
+       i + (kReadUnroll - 1) * 256 < n; i += stride) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u];
+  }
+  // a checksum compare against a run-time value keeps the loads live; a match (any
+  // lane of the block) only stores a flag
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == magic) out[blockIdx.x] = 1u;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmla_probe_mfma(int blocks, int iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return -1;
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters,
+                     out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int gmla_probe_read(const void* buf, size_t bytes, int blocks, unsigned* out, void* stream) {
+  const size_t chunk = (size_t)16 * 256 * kReadUnroll;
+  if (!buf || !out || blocks <= 0 || bytes == 0 || bytes % chunk || ((uintptr_t)buf % 16))
+    return -1;
+  hipLaunchKernelGGL(probe_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4*)buf, bytes / 16, 0x9e3779b9u, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"
