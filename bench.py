@@ -16,6 +16,7 @@ Profiling helpers (no compute of their own):
     python bench.py --only prefill|decode|layer|decode_long|copy --steps K
         run just that part, for rocprofv3 --kernel-trace or --pmc passes;
     python bench.py --summarize-stats DIR --name NAME --cmd "..."
+    python bench.py --summarize-mfma DIR --name NAME --cmd "..."
         turn rocprofv3 kernel statistics in DIR into profiles/NAME.md;
     python bench.py --summarize-traffic DIR_FETCH DIR_WRITE COPY_FETCH COPY_WRITE --kernel K --cmd "..."
         turn FETCH_SIZE / WRITE_SIZE passes (kernel and a 1 GiB copy for scale)
@@ -240,7 +241,7 @@ def _counter_per_dispatch(d, counter, match):
     return ordered[-1], len(ordered)  # last dispatch: warm caches, steady state
 
 
-def summarize_traffic(d_fetch, d_write, c_fetch, c_write, kernel, cmd):
+def summarize_traffic(d_fetch, d_write, c_fetch, c_write, kernel, cmd, key=None):
     kf, _ = _counter_per_dispatch(d_fetch, "FETCH_SIZE", kernel)
     kw, _ = _counter_per_dispatch(d_write, "WRITE_SIZE", kernel)
     cf, _ = _counter_per_dispatch(c_fetch, "FETCH_SIZE", "copyBuffer")
@@ -255,7 +256,8 @@ def summarize_traffic(d_fetch, d_write, c_fetch, c_write, kernel, cmd):
             data = json.load(f)
     except (OSError, ValueError):
         data = {}
-    data[kernel] = {"source_digest": source_digest(kernel), "bytes_per_launch": round(fetch + write),
+    key = key or kernel
+    data[key] = {"source_digest": source_digest(kernel), "bytes_per_launch": round(fetch + write),
                     "fetch_bytes": round(fetch), "write_bytes": round(write),
                     "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
                     "raw_fetch_kib": kf, "raw_write_kib": kw, "copy_fetch_kib": cf,
@@ -263,7 +265,7 @@ def summarize_traffic(d_fetch, d_write, c_fetch, c_write, kernel, cmd):
     os.makedirs(PROFILES, exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
-    print(json.dumps(data[kernel]))
+    print(json.dumps(data[key]))
 
 
 def summarize_counters(d, kernel, name, cmd):
@@ -289,6 +291,36 @@ def summarize_counters(d, kernel, name, cmd):
     print(out)
 
 
+def summarize_mfma(d, name, cmd):
+    """MFMA utilisation of every GPU kernel in a --pmc pass with SQ_VALU_MFMA_BUSY_CYCLES
+    and GRBM_GUI_ACTIVE: busy cycles summed over the 1024 SIMDs, against the dispatch's
+    active cycles (GRBM_GUI_ACTIVE sums the 8 XCDs), for the last dispatch of each."""
+    per = {}
+    for r in _read_csvs(d, "counter_collection.csv"):
+        k, did = _short(r["Kernel_Name"]), int(r["Dispatch_Id"])
+        slot = per.setdefault(k, {})
+        if slot.get("id", -1) < did:
+            per[k] = slot = {"id": did}
+        if slot["id"] == did:
+            slot[r["Counter_Name"]] = slot.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [f"# {name}", "", "Command:", "", "```", cmd, "```", "",
+             "MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs), "
+             "last dispatch of each kernel.", "",
+             "| kernel | MFMA instructions | MFMA busy | GRBM active | MFMA utilisation |",
+             "|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", 0)):
+        busy, act = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), v.get("GRBM_GUI_ACTIVE", 0.0)
+        if busy <= 0 or act <= 0:
+            continue
+        util = busy / (1024.0 * act / 8.0)
+        lines.append(f"| {k} | {v.get('SQ_INSTS_MFMA', 0):.4g} | {busy:.4g} | {act:.4g} | {util:.1%} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 # ----------------------------------------------------------------------------- main
 
 
@@ -304,16 +336,20 @@ def main():
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--summarize-mfma", metavar="DIR")
     ap.add_argument("--name")
     ap.add_argument("--kernel")
+    ap.add_argument("--key", help="record name in traffic.json (default: the kernel)")
     ap.add_argument("--cmd", default="")
     args = ap.parse_args()
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats, args.name, args.cmd)
     if args.summarize_traffic:
-        return summarize_traffic(*args.summarize_traffic, args.kernel, args.cmd)
+        return summarize_traffic(*args.summarize_traffic, args.kernel, args.cmd, args.key)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.kernel, args.name, args.cmd)
+    if args.summarize_mfma:
+        return summarize_mfma(args.summarize_mfma, args.name, args.cmd)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               f"sharding is described, not built.", file=sys.stderr)
