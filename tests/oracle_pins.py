@@ -51,6 +51,19 @@ def pin_causal_zero_upper(orc):
     assert np.all(A[~upper] > 0.0), "a visible key got zero weight"
 
 
+def pin_visible_pair_count(orc):
+    """Le Transformer et l'attention, 'Le coût quadratique': causal attention computes
+    about T^2/2 dot products -- exactly T(T+1)/2 visible (query, key) pairs, each with a
+    positive weight; without the mask all T^2."""
+    r = _rng(13)
+    for T in (1, 2, 7, 64, 100):
+        q, k, v = r.standard_normal((T, 4)), r.standard_normal((T, 4)), r.standard_normal((T, 4))
+        _, A = orc.attend_head(q, k, v, 0.5, True, want_probs=True)
+        assert int(np.count_nonzero(A)) == T * (T + 1) // 2
+        _, A = orc.attend_head(q, k, v, 0.5, False, want_probs=True)
+        assert int(np.count_nonzero(A)) == T * T
+
+
 def pin_three_token_example(orc):
     """Gated MLA, 'A small causal example': the lower-triangular pattern at T = 3,
     and every key visible in non-causal mode."""

@@ -168,3 +168,16 @@ def test_binding_rejects_cpu_tensors_and_mismatches():
         gm.gated_mla(x, *([torch.zeros(6, 6)] * 6), num_heads=4)
     with pytest.raises(TypeError):
         gm.gated_mla(x, *([torch.zeros(6, 6)] * 6), num_heads=2, causal="yes")
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
+def test_valid_call_without_a_device_returns_hip_error():
+    """Arguments that pass validation reach the launch; with no HIP device the launch
+    fails and the call returns GMLA_ERR_HIP instead of crashing."""
+    lib = gm.library()
+    assert _prefill() == -4
+    assert _chunk() == -4
+    assert _decode() == -4
+    assert lib.gmla_linear(1, 64, 64, 64, FAKE, FAKE, FAKE, None) == -4
+    assert lib.gmla_latent_expand(1, 64, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -4
+    assert lib.gmla_gate_out(1, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -4

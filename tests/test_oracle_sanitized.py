@@ -1,0 +1,29 @@
+"""The CPU oracle built with AddressSanitizer and UndefinedBehaviorSanitizer (gcc,
+host code only) and driven through every entry point by tests/oracle_sanitize_driver.c:
+no out-of-bounds access, leak, or undefined behaviour on any argument path."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_oracle_under_address_and_ub_sanitizers(tmp_path):
+    exe = tmp_path / "oracle_sanitized"
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-pthread",
+           os.path.join(ROOT, "oracle", "gmla_oracle.c"),
+           os.path.join(ROOT, "tests", "oracle_sanitize_driver.c"), "-lm", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 and "sanitizer" in r.stderr.lower():
+        pytest.skip("sanitizer runtime not available: " + r.stderr[-300:])
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    env.pop("LD_PRELOAD", None)
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "run clean" in run.stdout
