@@ -19,8 +19,11 @@
 //    lane-local as well.
 //  * Software pipeline: keys run one tile ahead of values.  Iteration j turns the
 //    scores of tile j into weights while the MFMAs of the next tile's scores
-//    (K_{j+1} Q^T) and of this tile's values (V_j^T P_j^T) issue, so the vector
-//    ALU work of the softmax overlaps the matrix cores.
+//    (K_{j+1} Q^T) and of this tile's values (V_j^T P_j^T) issue.  The iteration is a
+//    fixed sequence of 32 MFMA groups, each holding one MFMA, the LDS reads of the
+//    MFMA two groups on and a share of the softmax's vector work, kept in that order
+//    by scheduling fences; the matrix cores, the vector ALU and LDS then work side by
+//    side within a wave instead of in phases.
 //  * K and V tiles go from global memory straight into LDS (buffer loads with the
 //    LDS-direct form: no register staging, no vector ALU work).  Each load range ends
 //    at the last valid row, so rows past the sequence end arrive as zeros with no
@@ -42,6 +45,7 @@
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
 //    (shared L2), heaviest (longest-prefix) blocks first.
 #include <type_traits>
+#include <utility>
 
 #include "gmla_internal.h"
 
@@ -53,6 +57,7 @@ constexpr int BM = 128;         // queries per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int NTHREADS = 256;   // 4 waves
 constexpr int TILE = BN * HD;   // bf16 elements of one K or V tile (16 KB)
+constexpr int KR = 3;           // fragment ring: LDS reads run two MFMA groups ahead
 constexpr float kLazyRescale = 8.0f;   // raise the running max only past 2^8 growth
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
@@ -68,6 +73,20 @@ template <int B> __device__ __forceinline__ bf16* v_buf() { return B ? lds_v1 : 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+template <int... Is, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, in order
+template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+// Hides a value from loop-invariant code motion (address arithmetic is redone per use).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Swizzles of the 16-byte chunk index (8 channels) inside a 256-byte tile row.
 // K: 16 consecutive rows read the same logical chunk -> 16 distinct bank groups.
@@ -253,9 +272,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   float mt_cur = tile_max(s_cur);
   __syncthreads();  // every wave has read K buffer 0 before iteration 0 refills it
 
-  // One iteration: weights of tile j, values of tile j, scores of tile j+1.
-  //   NEXT: 0 = there is a next tile (masked if it straddles the diagonal or the end),
-  //         2 = tile j is the last one.
+  // K fragment of (32-key half sub, k-step ks): row 32 sub + l32, logical chunk
+  // 2 ks + hh, i.e. byte 8192 sub + (kfrag ^ 32 ks) of the tile (the swizzle only moves
+  // bits 4..7).
+  const int kfrag = l32 * 256 + ((hh ^ (l32 & 15)) << 4);
+
+  // One iteration: weights of tile j, values of tile j, scores of tile j+1, as a fixed
+  // interleave of 32 MFMA groups (the fences keep the order): each group issues one
+  // MFMA, requests the LDS fragments of the MFMA two groups on, and carries a share of
+  // the vector work (exponentials of tile j, then the maximum of tile j+1), so the
+  // vector ALU and the LDS reads run under the matrix cores.
+  //   NEXT: 0 = there is a next tile, 2 = tile j is the last one.
   //   PAR = j mod 2 selects the buffers: K_{j+1} and V_j are read, K_{j+2} and V_{j+1}
   //   are loaded into the buffers K_j and V_{j-1} used.
   auto step = [&](int j, auto next_kind, auto parity) __attribute__((always_inline)) {
@@ -281,43 +308,104 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       load_k(j + 2, BP{});
       load_v(j + 1, BQ{});
     }
-    // scores of the next tile (its K is already in LDS)
-    f32x16 s_next[2];
-    if (NEXT != 2) scores(BQ{}, s_next);
-    // weights, rounded to bf16 as the B operand of O^T = V^T P^T
-    bf16x8 p[2][2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s_cur[sub][half * 8 + e], c2, -m_run));
-          const float p1 = fast_exp2(__builtin_fmaf(s_cur[sub][half * 8 + e + 1], c2, -m_run));
-          bf16x2 pp;
-          pp[0] = (bf16)p0;
-          pp[1] = (bf16)p1;
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
-          p[sub][half][e] = pp[0];
-          p[sub][half][e + 1] = pp[1];
-        }
-    // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16), 4 blocks of 32 channels
-    const bf16* vtile = v_buf<PAR>();
-#pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
-      const bf16x8 pb = p[kstep >> 1][kstep & 1];
-#pragma unroll
-      for (int dblk = 0; dblk < 4; ++dblk) {
-        const bf16* src = vtile + kstep * 16 * HD + v_off[dblk];
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src + 8 * HD));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o_acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o_acc[dblk], 0, 0, 0);
-      }
-    }
-    if (NEXT != 2) {
+    const char* kt = (const char*)k_buf<1 - PAR>();
+    const bf16* vt = v_buf<PAR>();
+    const int kfl = opaque(kfrag);
+    auto kread = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(I)::value;
+      return *(const bf16x8*)(kt + (i >> 3) * 8192 + (kfl ^ ((i & 7) << 5)));
+    };
+    auto vread = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(I)::value;
+      const bf16* src = vt + (i >> 2) * 16 * HD + v_off[i & 3];
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src + 8 * HD));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // weights of two scores of tile j, rounded to bf16 (B operand of O^T = V^T P^T):
+    // unit u covers elements 2 (u mod 4) + {0, 1} of half (u / 4) mod 2 of sub u / 8,
+    // i.e. word u mod 4 of k-step u / 4
+    uint32_t pw[4][4];
+    auto eunit = [&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      constexpr int sub = u >> 3, idx = ((u >> 2) & 1) * 8 + (u & 3) * 2;
+      const float p0 = fast_exp2(__builtin_fmaf(s_cur[sub][idx], c2, -m_run));
+      const float p1 = fast_exp2(__builtin_fmaf(s_cur[sub][idx + 1], c2, -m_run));
+      bf16x2 pp;
+      pp[0] = (bf16)p0;
+      pp[1] = (bf16)p1;
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
+      uint32_t w = __builtin_bit_cast(uint32_t, pp);
+      // pin the unit where it is placed (the compiler would otherwise sink it past the
+      // mask branch, next to its first use)
+      asm volatile("" : "+v"(w), "+v"(l_run));
+      pw[u >> 2][u & 3] = w;
+    };
+    auto pv_mfma = [&](auto I, const bf16x8& vf) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      u32x4 w;
+      w[0] = pw[i >> 2][0];
+      w[1] = pw[i >> 2][1];
+      w[2] = pw[i >> 2][2];
+      w[3] = pw[i >> 2][3];
+      o_acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, w), o_acc[i & 3], 0, 0, 0);
+    };
+
+    if constexpr (NEXT == 2) {
+      // last tile: weights, then values
+      static_for<16>([&](auto U) { eunit(U); });
+      static_for<16>([&](auto I) { pv_mfma(I, vread(I)); });
+    } else {
+      f32x16 s_next[2];
+      s_next[0] = f32x16{};
+      s_next[1] = f32x16{};
+      bf16x8 kf[KR], vf[KR];
+      static_for<KR - 1>([&](auto I) { kf[decltype(I)::value] = kread(I); });
+      __builtin_amdgcn_sched_barrier(0);
+      // groups 0..15: scores of tile j+1 (K_{j+1} Q^T), weights units 0..9
+      static_for<16>([&](auto G) {
+        constexpr int g = decltype(G)::value;
+        s_next[g >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g % KR], qf[g & 7], s_next[g >> 3], 0, 0, 0);
+        constexpr int nx = g + KR - 1;  // fragment requested in this group
+        if constexpr (nx < 16)
+          kf[nx % KR] = kread(std::integral_constant<int, nx>{});
+        else
+          vf[(nx - 16) % KR] = vread(std::integral_constant<int, nx - 16>{});
+        static_for<10>([&](auto U) {
+          if constexpr ((decltype(U)::value * 16) / 10 == g) eunit(U);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // the tiles that straddle the diagonal or the end (waits for the scores)
       if (j + 1 >= mask_from) mask(s_next, j + 1);
-      mt_cur = tile_max(s_next);
+      __builtin_amdgcn_sched_barrier(0);
+      // groups 16..21: values of tile j, weights units 10..15
+      static_for<6>([&](auto G) {
+        constexpr int g = decltype(G)::value;
+        pv_mfma(G, vf[g % KR]);
+        vf[(g + KR - 1) % KR] = vread(std::integral_constant<int, g + KR - 1>{});
+        eunit(std::integral_constant<int, 10 + g>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // groups 22..31: values of tile j, maximum of tile j+1
+      float mx0 = s_next[0][0], mx1 = s_next[1][0];
+      static_for<10>([&](auto G) {
+        constexpr int g = decltype(G)::value + 6;
+        pv_mfma(std::integral_constant<int, g>{}, vf[g % KR]);
+        if constexpr (g + KR - 1 < 16) vf[(g + KR - 1) % KR] = vread(std::integral_constant<int, g + KR - 1>{});
+        if constexpr (g < 14) {
+          constexpr int c = g - 6;  // 0..7: four-element chunk c mod 4 of sub c / 4
+          if constexpr (c < 4) {
+            mx0 = fmaxf(fmaxf(mx0, s_next[0][4 * c]), s_next[0][4 * c + 1]);
+            mx0 = fmaxf(fmaxf(mx0, s_next[0][4 * c + 2]), s_next[0][4 * c + 3]);
+          } else {
+            mx1 = fmaxf(fmaxf(mx1, s_next[1][4 * (c - 4)]), s_next[1][4 * (c - 4) + 1]);
+            mx1 = fmaxf(fmaxf(mx1, s_next[1][4 * (c - 4) + 2]), s_next[1][4 * (c - 4) + 3]);
+          }
+        }
+        if constexpr (g == 14) mt_cur = swap_halves_max(fmaxf(mx0, mx1)) * c2;
+        __builtin_amdgcn_sched_barrier(0);
+      });
       tile_barrier();
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];
