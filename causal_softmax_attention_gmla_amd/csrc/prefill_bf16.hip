@@ -43,7 +43,8 @@
 //    query i sits at position i + Tk - T and sees the keys up to there ("Kimi K2 -
 //    Construct causal mask": positions continue from the cached length).
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
-//    (shared L2), heaviest (longest-prefix) blocks first.
+//    (shared L2); an XCD's heads go in groups of four whose query blocks launch
+//    heaviest (longest prefix) first across the group.
 #include <type_traits>
 #include <utility>
 
@@ -58,6 +59,7 @@ constexpr int BN = 64;          // keys per tile
 constexpr int NTHREADS = 256;   // 4 waves
 constexpr int TILE = BN * HD;   // bf16 elements of one K or V tile (16 KB)
 constexpr int KR = 3;           // fragment ring: LDS reads run two MFMA groups ahead
+constexpr int kHeadGroup = 4;   // heads whose query blocks are interleaved in launch order
 constexpr float kLazyRescale = 8.0f;   // raise the running max only past 2^8 growth
 constexpr int kBufferDword3 = 0x00020000;  // raw buffer resource, 32-bit data format
 
@@ -122,12 +124,29 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, bf16* dst, 
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb,
                                                                    int total) {
 
-  // ---- workgroup -> (head, query block): same-head blocks on one XCD, heavy first
+  // ---- workgroup -> (head, query block).  Workgroups are dealt to the XCDs round-robin
+  // and each XCD takes a contiguous set of heads (their K/V then share that XCD's L2).
+  // Within an XCD, heads go in groups of kHeadGroup and a group's query blocks in order
+  // of decreasing work across its heads: launched in that order, the causal blocks
+  // (2 to 2 nqb key tiles each) fill the XCD's workgroup slots evenly, where head by head
+  // order left slots idle near each head's end.
   const int bid = blockIdx.x;
   const int per_xcd = total / kNumXcd;
-  const int L = bid < per_xcd * kNumXcd ? (bid % kNumXcd) * per_xcd + bid / kNumXcd : bid;
-  const int head_lin = L / nqb;
-  const int qb = a.causal ? nqb - 1 - (L % nqb) : (L % nqb);
+  int head_lin, rank;
+  if (bid < per_xcd * kNumXcd && per_xcd % nqb == 0) {
+    const int x = bid % kNumXcd, i = bid / kNumXcd;
+    const int hx = per_xcd / nqb;  // heads per XCD
+    const int G = min(kHeadGroup, hx);
+    const int g = i / (G * nqb), j = i % (G * nqb);
+    const int gg = min(G, hx - g * G);  // heads in this group
+    rank = j / gg;
+    head_lin = x * hx + g * G + j % gg;
+  } else {
+    const int L = bid < per_xcd * kNumXcd ? (bid % kNumXcd) * per_xcd + bid / kNumXcd : bid;
+    head_lin = L / nqb;
+    rank = L % nqb;
+  }
+  const int qb = a.causal ? nqb - 1 - rank : rank;
   const int b = head_lin / a.H;
   const int h = head_lin % a.H;
   const int q0 = qb * BM;
@@ -136,7 +155,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int off = a.Tk - a.T;    // position of query 0
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
