@@ -19,9 +19,11 @@ def test_prefill_b2_t4096_sampled():
     dev = need_gpu()
     announce("prefill_b2_t4096 full size, sampled rows")
     q, k, v, _ = I.workload_inputs("prefill_b2_t4096", dev)
-    out = gm.attend_prefill(q, k, v)
-    torch.cuda.synchronize()
     B, T, H, D = q.shape
+    out = torch.full((B, T, H * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.attend_prefill(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "some (head, query block) was never written"
     r = np.random.default_rng(11)
     heads = [(0, 0), (1, H - 1)] + [(int(r.integers(B)), int(r.integers(H))) for _ in range(4)]
     rows = sorted(set([0, 1, 31, 32, 63, 64, 127, 128, 129, 1000, 2047, 2048, 4094, 4095]

@@ -61,6 +61,21 @@ def test_prefill_bf16_mfma_shapes(T, causal):
     check_rows_rel(host(out), _oracle_prefill(q, k, v, g, causal), 128)
 
 
+@pytest.mark.parametrize("B,T,H", [(1, 256, 40), (1, 512, 24), (2, 1024, 8), (1, 384, 48)])
+def test_prefill_bf16_launch_groups(B, T, H):
+    """Shapes whose query blocks split evenly over the 8 XCDs with 5, 3, 2 and 6 heads per
+    XCD: the launch order interleaves heads in groups (a partial last group for 5 and 6),
+    and every (head, query block) must still be computed exactly once."""
+    dev = need_gpu()
+    announce(f"prefill bf16 launch groups B={B} T={T} H={H}")
+    q, k, v, _ = I.prefill_inputs(B, T, H, 128, torch.bfloat16, dev, seed=3000 + H)
+    out = torch.full((B, T, H * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.attend_prefill(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, None, True), 128)
+
+
 # ---------------------------------------------------------------- chunk after a cache
 
 
