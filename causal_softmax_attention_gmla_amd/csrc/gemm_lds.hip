@@ -254,24 +254,43 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
     }
   }
 
-  // ---- epilogue: D[n][m] holds, in lane (m = l32), rows n = 8 (r/4) + 4 hh + r%4:
-  // four consecutive n per register quad -> one 8-byte store each
+  // ---- epilogue: D[n][m] holds, in lane (m = l32), rows n = 8 (r/4) + 4 hh + r%4, i.e.
+  // four consecutive n of one row m per register quad.  Stored as they are, each store
+  // instruction would touch 32 rows with 16 bytes apiece; instead the tile goes through
+  // LDS in chunks of 64 columns: every wave writes its part of the chunk into the first
+  // X stage buffer (now idle; rows of 128 bytes, 16-byte unit q of row r at
+  // q ^ ((r >> 1) & 7)), then the workgroup stores whole 128-byte row segments.
+  static_assert(BN % 64 == 0, "64-column chunks");
+  char* const stage = (char*)xbuf(B0{});  // BM rows x 64 bf16
 #pragma unroll
-  for (int j = 0; j < C::FM; ++j) {
-    const int m = m0 + wm * C::TM + j * 32 + l32;
-    if (m >= M) continue;
-    bf16* yrow = Y + (int64_t)m * N;
+  for (int c = 0; c < BN / 64; ++c) {
+    lds_barrier();  // every wave is done with the stage buffer (main loop or last chunk)
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i)
+    for (int i = 0; i < C::FN; ++i) {
+      const int ncol = wn * C::TN + i * 32;  // first tile column of fragment i
+      if (ncol < 64 * c || ncol >= 64 * c + 64) continue;  // uniform per wave
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + wn * C::TN + i * 32 + 8 * r4 + 4 * hh;
-        if (n >= N) continue;
-        u32x2 v;
-        v[0] = pack_bf16x2(acc[i][j][4 * r4 + 0], acc[i][j][4 * r4 + 1]);
-        v[1] = pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
-        *(u32x2*)(yrow + n) = v;
+      for (int j = 0; j < C::FM; ++j) {
+        const int row = wm * C::TM + j * 32 + l32;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int col = ncol - 64 * c + 8 * r4 + 4 * hh;  // 0..63
+          u32x2 v;
+          v[0] = pack_bf16x2(acc[i][j][4 * r4 + 0], acc[i][j][4 * r4 + 1]);
+          v[1] = pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+          *(u32x2*)(stage + row * 128 + (((col >> 3) ^ ((row >> 1) & 7)) << 4) + (col & 4) * 2) = v;
+        }
       }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < BM * 8 / C::NT; ++k) {
+      const int piece = tid + k * C::NT;
+      const int row = piece >> 3, q = piece & 7;
+      const int m = m0 + row, n = n0 + 64 * c + 8 * q;
+      const u32x4 v = *(const u32x4*)(stage + row * 128 + ((q ^ ((row >> 1) & 7)) << 4));
+      if (m < M && n < N) *(u32x4*)(Y + (int64_t)m * N + n) = v;
+    }
   }
 }
 
@@ -303,7 +322,7 @@ hipError_t launch_cfg(void (*kernel)(GemmArgs, int, int, int), const GemmArgs& p
 bool gemm_lds_supported(const GemmArgs& p) {
   const auto al = [](const void* q, uintptr_t a) { return ((uintptr_t)q % a) == 0; };
   if (p.g || p.K % BK || p.N % 8 || (p.w2 && p.N2 % 8)) return false;
-  if (!al(p.x, 16) || !al(p.w, 16) || !al(p.y, 8) || (p.w2 && (!al(p.w2, 16) || !al(p.y2, 8))))
+  if (!al(p.x, 16) || !al(p.w, 16) || !al(p.y, 16) || (p.w2 && (!al(p.w2, 16) || !al(p.y2, 16))))
     return false;
   // byte offsets inside one block's rows are 32-bit
   return (int64_t)256 * p.K * 2 < ((int64_t)1 << 31);
