@@ -445,13 +445,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     step(j, Last{}, B0{});
   }
 
-  // ---- epilogue: normalise, gate, round, store [B, T, H*128]
-  if (tq >= T) return;
+  // ---- epilogue: normalise, gate, round, store [B, T, H*128].  O^T leaves a lane four
+  // consecutive channels of one query per register quad; stored directly, each store
+  // instruction would touch 32 query rows.  Instead each wave puts its 32 rows x 128
+  // channels (bf16, 8 KB) in its own quarter of the two K buffers, which no wave reads
+  // after the second-to-last tile, and stores whole 256-byte rows from there.  Row r's
+  // 16-byte unit u sits at unit u ^ (r mod 16), so neither side meets bank conflicts.
   const float l_tot = swap_halves_sum(l_run);
   const float inv = 1.0f / l_tot;
-  const int64_t row = ((int64_t)b * T + tq) * ((int64_t)a.H * HD) + (int64_t)h * HD;
-  bf16* __restrict__ out = (bf16*)a.o + row;
-  const bf16* __restrict__ gate = a.g ? (const bf16*)a.g + row : nullptr;
+  const int64_t hd = (int64_t)a.H * HD;
+  const bf16* __restrict__ gate = a.g ? (const bf16*)a.g + ((int64_t)b * T + tq) * hd + (int64_t)h * HD
+                                      : nullptr;
+  char* const ep = (char*)(wave < 2 ? lds_k0 : lds_k1) + (wave & 1) * 8192;
 #pragma unroll
   for (int dblk = 0; dblk < 4; ++dblk)
 #pragma unroll
@@ -461,7 +466,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       float v1 = o_acc[dblk][4 * r4 + 1] * inv;
       float v2 = o_acc[dblk][4 * r4 + 2] * inv;
       float v3 = o_acc[dblk][4 * r4 + 3] * inv;
-      if (gate) {
+      if (gate && tq < T) {
         const u32x2 gw = *(const u32x2*)(gate + d);
         v0 *= sigmoidf_(bf16_lo(gw[0]));
         v1 *= sigmoidf_(bf16_hi(gw[0]));
@@ -471,8 +476,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       u32x2 w;
       w[0] = pack_bf16x2(v0, v1);
       w[1] = pack_bf16x2(v2, v3);
-      *(u32x2*)(out + d) = w;
+      *(u32x2*)(ep + l32 * 256 + (((d >> 3) ^ (l32 & 15)) << 4) + (d & 4) * 2) = w;
     }
+  bf16* __restrict__ out = (bf16*)a.o + ((int64_t)b * T + wq0) * hd + (int64_t)h * HD;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int piece = lane + 64 * k;
+    const int r = piece >> 4, u = piece & 15;  // query wq0 + r, channels 8u .. 8u+7
+    const u32x4 v = *(const u32x4*)(ep + r * 256 + ((u ^ (r & 15)) << 4));
+    if (wq0 + r < T) *(u32x4*)(out + r * hd + 8 * u) = v;
+  }
 }
 
 }  // namespace
