@@ -249,6 +249,25 @@ def test_linear(M, N, K, dtype):
         check_rows_rel(host(y), ref, N)
 
 
+@pytest.mark.parametrize("offset", [0, 4, 8])
+def test_linear_output_alignment(offset):
+    """Output buffers 16-, 8- and 16-byte aligned (bf16 element offsets 0, 4, 8 into one
+    allocation): the LDS-pipelined kernel stores 16 bytes per lane and takes only
+    16-byte-aligned outputs; the others go to the register-staged kernel.  Both match."""
+    dev = need_gpu()
+    M, N, K = 512, 1024, 256
+    announce(f"linear output offset {offset}")
+    x = I.normal((M, K), torch.bfloat16, dev, seed=4100)
+    w = I.normal((N, K), torch.bfloat16, dev, seed=4101, std=K ** -0.5)
+    buf = torch.full((M * N + 16,), float("nan"), dtype=torch.bfloat16, device=dev)
+    y = buf[offset:offset + M * N].view(M, N)
+    gm.linear(x, w, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    assert torch.isnan(buf[:offset]).all() and torch.isnan(buf[offset + M * N:]).all()
+    check_rows_rel(host(y), oracle.linear(host(x), host(w)), N)
+
+
 @pytest.mark.parametrize("M,N,K", [(2000, 8200, 320), (2048, 8192, 64), (1500, 11000, 192)])
 def test_linear_wide_ragged(M, N, K):
     """Wide bf16 products (enough 256 x 128 tiles to take the multi-stage kernel): M and N
