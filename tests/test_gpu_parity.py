@@ -61,6 +61,25 @@ def test_prefill_bf16_mfma_shapes(T, causal):
     check_rows_rel(host(out), _oracle_prefill(q, k, v, g, causal), 128)
 
 
+@pytest.mark.parametrize("T", [65, 300])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_bf16_writes_only_its_output(T, causal):
+    """Ragged last query blocks: the output goes to a view inside a larger NaN-filled
+    buffer; every output element is written and nothing around it is."""
+    dev = need_gpu()
+    announce(f"prefill bf16 output bounds T={T} causal={causal}")
+    B, H, D = 2, 3, 128
+    q, k, v, _ = I.prefill_inputs(B, T, H, D, torch.bfloat16, dev, seed=5000 + T)
+    n = B * T * H * D
+    buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = buf[2048:2048 + n].view(B, T, H * D)
+    gm.attend_prefill(q, k, v, causal=causal, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    assert torch.isnan(buf[:2048]).all() and torch.isnan(buf[2048 + n:]).all()
+    check_rows_rel(host(out), _oracle_prefill(q, k, v, None, causal), 128)
+
+
 @pytest.mark.parametrize("B,T,H", [(1, 256, 40), (1, 512, 24), (2, 1024, 8), (1, 384, 48)])
 def test_prefill_bf16_launch_groups(B, T, H):
     """Shapes whose query blocks split evenly over the 8 XCDs with 5, 3, 2 and 6 heads per
