@@ -15,7 +15,8 @@
 //    c ^ ((r >> 1) & 7), which makes the fragment reads free of bank conflicts.
 //  * The MFMA computes D = W X^T (v_mfma_f32_32x32x16_bf16, A = 32 rows of W, B = 32
 //    rows of X): a lane then holds four consecutive output columns n of one output row
-//    m per register quad, so results leave as 8-byte stores.
+//    m per register quad; the tile is packed to bf16 in LDS and leaves as 16-byte
+//    stores of whole 128-byte row segments.
 //  * Workgroups are dealt so that the M blocks of one N block run on the same XCD:
 //    the W tile they share is fetched from HBM once into that XCD's L2.
 #include <type_traits>
@@ -74,6 +75,10 @@ __shared__ __align__(16) bf16 wide_x0[256 * BK];
 __shared__ __align__(16) bf16 wide_x1[256 * BK];
 __shared__ __align__(16) bf16 wide_w0[192 * BK];
 __shared__ __align__(16) bf16 wide_w1[192 * BK];
+__shared__ __align__(16) bf16 deep_x0[256 * BK];
+__shared__ __align__(16) bf16 deep_x1[256 * BK];
+__shared__ __align__(16) bf16 deep_w0[384 * BK];
+__shared__ __align__(16) bf16 deep_w1[384 * BK];
 __shared__ __align__(16) bf16 narrow_x0[64 * BK];
 __shared__ __align__(16) bf16 narrow_x1[64 * BK];
 __shared__ __align__(16) bf16 narrow_x2[64 * BK];
@@ -87,6 +92,10 @@ template <int BM, int BN, int S> struct StageSet;
 template <> struct StageSet<256, 192, 2> {
   template <int B> static __device__ __forceinline__ bf16* x() { return B == 0 ? wide_x0 : wide_x1; }
   template <int B> static __device__ __forceinline__ bf16* w() { return B == 0 ? wide_w0 : wide_w1; }
+};
+template <> struct StageSet<256, 384, 2> {
+  template <int B> static __device__ __forceinline__ bf16* x() { return B == 0 ? deep_x0 : deep_x1; }
+  template <int B> static __device__ __forceinline__ bf16* w() { return B == 0 ? deep_w0 : deep_w1; }
 };
 template <> struct StageSet<64, 64, 4> {
   template <int B> static __device__ __forceinline__ bf16* x() {
@@ -143,27 +152,32 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
   // Load u of a wave fills 8 LDS rows (1 KB) in physical chunk order: lane i writes
   // row 8 (wave * L + u) + i / 8, physical chunk i mod 8, i.e. logical chunk
   // (i mod 8) ^ ((row >> 1) & 7) of that row; the stage's k offset is the scalar part.
+  // The 256 x 384 tile keeps no offsets in registers (its accumulators take 192 of the
+  // wave's 256): they are recomputed at each stage from the lane index.
+  constexpr bool kKeepOffsets = BN < 384;
   uint32_t xo[C::XL], wo[C::WL];
+  auto offset = [&](int row, int ln) __attribute__((always_inline)) {
+    return (uint32_t)(row * K * 2 + (((ln & 7) ^ ((row >> 1) & 7)) << 4));
+  };
+  if (kKeepOffsets) {
 #pragma unroll
-  for (int u = 0; u < C::XL; ++u) {
-    const int row = 8 * (wave * C::XL + u) + (lane >> 3);
-    xo[u] = (uint32_t)(row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
-  }
+    for (int u = 0; u < C::XL; ++u) xo[u] = offset(8 * (wave * C::XL + u) + (lane >> 3), lane);
 #pragma unroll
-  for (int u = 0; u < C::WL; ++u) {
-    const int row = 8 * (wave * C::WL + u) + (lane >> 3);
-    wo[u] = (uint32_t)(row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) << 4));
+    for (int u = 0; u < C::WL; ++u) wo[u] = offset(8 * (wave * C::WL + u) + (lane >> 3), lane);
   }
   auto load_stage = [&](int kt, auto b) __attribute__((always_inline)) {
     const int koff = kt * BK * 2;
+    const int ln = kKeepOffsets ? lane : opaque(lane);
 #pragma unroll
     for (int u = 0; u < C::XL; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(xbuf(b) + (wave * C::XL + u) * 512),
-                                               16, xo[u], koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_void_t*)(xbuf(b) + (wave * C::XL + u) * 512), 16,
+          kKeepOffsets ? xo[u] : offset(8 * (wave * C::XL + u) + (ln >> 3), ln), koff, 0, 0);
 #pragma unroll
     for (int u = 0; u < C::WL; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t*)(wbuf(b) + (wave * C::WL + u) * 512),
-                                               16, wo[u], koff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (lds_void_t*)(wbuf(b) + (wave * C::WL + u) * 512), 16,
+          kKeepOffsets ? wo[u] : offset(8 * (wave * C::WL + u) + (ln >> 3), ln), koff, 0, 0);
   };
 
   // Fragment reads: row l32 of a 32-row group, logical chunk 2 ks + hh, at byte
@@ -300,6 +314,10 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_wide_kernel(GemmArgs p, int n
                                                                int total) {
   gemm_lds_body<256, 192, 2, 4, 2>(p, nb1, nmb, total);
 }
+__global__ __launch_bounds__(512, 1) void gemm_lds_deep_kernel(GemmArgs p, int nb1, int nmb,
+                                                               int total) {
+  gemm_lds_body<256, 384, 2, 2, 4>(p, nb1, nmb, total);
+}
 __global__ __launch_bounds__(256, 2) void gemm_lds_narrow_kernel(GemmArgs p, int nb1, int nmb,
                                                                  int total) {
   gemm_lds_body<64, 64, 4, 2, 2>(p, nb1, nmb, total);
@@ -329,11 +347,21 @@ bool gemm_lds_supported(const GemmArgs& p) {
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& p, hipStream_t s) {
+  // Deep products (K >= 1024) with enough 256 x 384 tiles to fill the CUs: 8 waves of
+  // 128 x 96, 2 stages (160 KB of LDS, one workgroup per CU); per flop they move 29% fewer
+  // tile bytes global -> LDS and read 30% fewer fragment bytes than 256 x 192 tiles
+  // (measured on 2048 x 12288 x 12288: 1076 -> 1243 TFLOP/s), but with K = 512 their
+  // prologue weighs more (775 -> 701), so the latent expansion keeps the wide tiles.
   // Wide outputs: 256 x 192 tiles, 8 waves of 64 x 96, 2 stages (112 KB of LDS, one
   // workgroup per CU); measured against 256 x 128 tiles with 3 stages: 5% faster on the
   // 12288-deep projections, 16% on the 512-deep latent expansion.  Narrow outputs (too
   // few wide tiles to fill 256 CUs): 64 x 64 tiles, 4 waves of 32 x 32, 4 stages (64 KB,
   // two workgroups per CU).
+  const long deep = (long)((p.M + 255) / 256) *
+                    ((p.N + 383) / 384 + (p.w2 ? (p.N2 + 383) / 384 : 0));
+  if (deep >= 256 && p.K >= 1024 && p.N % 384 == 0 && (!p.w2 || p.N2 % 384 == 0) &&
+      (int64_t)384 * p.K * 2 < ((int64_t)1 << 31))
+    return launch_cfg<256, 384, 512>(gemm_lds_deep_kernel, p, s);
   const long big = (long)((p.M + 255) / 256) *
                    ((p.N + 191) / 192 + (p.w2 ? (p.N2 + 191) / 192 : 0));
   if (big >= 512) return launch_cfg<256, 192, 512>(gemm_lds_wide_kernel, p, s);

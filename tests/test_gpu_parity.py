@@ -288,11 +288,12 @@ def test_linear_output_alignment(offset):
 
 
 @pytest.mark.parametrize("M,N,K", [(2000, 8200, 320), (2048, 8192, 64), (1500, 11000, 192)])
-def test_linear_wide_ragged(M, N, K):
-    """Wide bf16 products (enough 256 x 128 tiles to take the multi-stage kernel): M and N
-    not multiples of the tile, K one stage or a few; sampled output rows."""
+def test_linear_mid_ragged(M, N, K):
+    """Mid-size bf16 products (too few 256 x 192 tiles for the wide kernel, so the 64 x 64
+    four-stage kernel): M and N not multiples of the tile, K one stage or a few; sampled
+    output rows."""
     dev = need_gpu()
-    announce(f"linear wide {M}x{N}x{K}")
+    announce(f"linear mid {M}x{N}x{K}")
     x = I.normal((M, K), torch.bfloat16, dev, seed=4300 + K)
     w = I.normal((N, K), torch.bfloat16, dev, seed=4301 + K, std=K ** -0.5)
     y = gm.linear(x, w)
@@ -302,8 +303,46 @@ def test_linear_wide_ragged(M, N, K):
     check_rows_rel(host(y)[rows], ref, N)
 
 
+@pytest.mark.parametrize("M,N,K", [(2000, 12200, 320), (2048, 12296, 1024), (1999, 12288, 1088),
+                                   (2048, 12288, 1024)])
+def test_linear_large_tiles_ragged(M, N, K):
+    """Products with enough large tiles to fill the CUs: 256 x 192 tiles (the first two: N
+    not a multiple of 192, or K deep but N not a multiple of 384) and 256 x 384 tiles (K >=
+    1024 and N a multiple of 384; M not a multiple of 256, and an odd number of 64-deep
+    stages).  The output starts as NaN: every element is written; sampled rows match the
+    oracle across the full width."""
+    dev = need_gpu()
+    announce(f"linear large tiles {M}x{N}x{K}")
+    x = I.normal((M, K), torch.bfloat16, dev, seed=4400 + K)
+    w = I.normal((N, K), torch.bfloat16, dev, seed=4401 + K, std=K ** -0.5)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.linear(x, w, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    rows = sorted(set(list(range(0, M, 89)) + [M - 1, M - 2, 255, 256, 1791, 1792]))
+    check_rows_rel(host(y)[rows], oracle.linear(host(x)[rows], host(w)), N)
+
+
+@pytest.mark.parametrize("M,dc,dm", [(2000, 320, 6152), (2048, 1024, 6144)])
+def test_latent_expand_large_tiles(M, dc, dm):
+    """Both outputs of one launch in the large-tile kernels: 256 x 192 tiles with widths
+    not a tile multiple, and 256 x 384 tiles (a 1024-wide latent); sampled rows."""
+    dev = need_gpu()
+    announce(f"latent_expand large tiles {M}x{dm}x{dc}")
+    c = I.normal((M, dc), torch.bfloat16, dev, seed=4120 + dc)
+    wk = I.normal((dm, dc), torch.bfloat16, dev, seed=4121 + dc, std=dc ** -0.5)
+    wv = I.normal((dm, dc), torch.bfloat16, dev, seed=4122 + dc, std=dc ** -0.5)
+    K, V = gm.latent_expand(c, wk, wv)
+    torch.cuda.synchronize()
+    rows = sorted(set(list(range(0, M, 127)) + [M - 1, 255, 256]))
+    for got, w in ((K, wk), (V, wv)):
+        assert not torch.isnan(got).any()
+        check_rows_rel(host(got)[rows], oracle.linear(host(c)[rows], host(w)), dm)
+
+
 def test_latent_expand_wide_ragged():
-    """Both outputs of one launch in the multi-stage kernel, widths not a tile multiple."""
+    """Both outputs of one launch in the 64 x 64 four-stage kernel, widths not a tile
+    multiple."""
     dev = need_gpu()
     announce("latent_expand wide 2000x4104x320")
     M, dc, dm = 2000, 320, 4104
