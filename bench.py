@@ -218,7 +218,7 @@ def _short(name: str) -> str:
     return name if len(name) < 90 else name[:87] + "..."
 
 
-def summarize_stats(d, name, cmd):
+def summarize_stats(d, name, cmd, window=None):
     rows = _read_csvs(d, "kernel_stats.csv")
     if not rows:
         sys.exit(f"no *kernel_stats.csv under {d}")
@@ -229,6 +229,26 @@ def summarize_stats(d, name, cmd):
         ns = lambda k: float(r.get(k, "nan")) / 1e3  # noqa: E731
         lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {ns('AverageNs'):.1f} | "
                      f"{ns('MinNs'):.1f} | {ns('MaxNs'):.1f} | {float(r['Percentage']):.2f} |")
+    if window:
+        # The statistics above average every dispatch, the warm-up calls included (a fresh
+        # GPU runs its first calls slower while the clocks settle); the timed region of
+        # bench.py is dispatches W .. W+K-1 of each kernel, in launch order.
+        w, k = window
+        per = {}
+        for r in _read_csvs(d, "kernel_trace.csv"):
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", f"Dispatches {w} .. {w + k - 1} of each library kernel launched at least "
+                      f"{w + k} times (the timed calls after {w} warm-up calls), from the kernel "
+                      f"trace:", "",
+                  "| kernel | warm-up average (us) | timed average (us) |", "|---|---|---|"]
+        for kname, v in sorted(per.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+            if len(v) < w + k or "gmla" not in kname:
+                continue
+            v.sort()
+            warm = sum(x[1] for x in v[:w]) / max(w, 1) / 1e3
+            timed = sum(x[1] for x in v[w:w + k]) / k / 1e3
+            lines.append(f"| {_short(kname)} | {warm:.1f} | {timed:.1f} |")
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"{name}.md")
     with open(out, "w") as f:
@@ -336,12 +356,16 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # A fresh GPU runs the first few dozen prefill calls up to 30% slower while its clocks
+    # settle under sustained matrix-core load; 60 untimed calls reach the steady state.
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--all", action="store_true", help="also time the layer and the 131072-key decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--only", choices=["prefill", "decode", "layer", "decode_long", "copy"])
     ap.add_argument("--summarize-stats", metavar="DIR")
+    ap.add_argument("--timed-window", nargs=2, type=int, metavar=("W", "K"),
+                    help="with --summarize-stats: also average dispatches W .. W+K-1 per kernel")
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--summarize-mfma", metavar="DIR")
@@ -351,7 +375,7 @@ def main():
     ap.add_argument("--cmd", default="")
     args = ap.parse_args()
     if args.summarize_stats:
-        return summarize_stats(args.summarize_stats, args.name, args.cmd)
+        return summarize_stats(args.summarize_stats, args.name, args.cmd, args.timed_window)
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.kernel, args.cmd, args.key)
     if args.summarize_counters:
@@ -456,7 +480,7 @@ def main():
             lavg, _, _ = time_calls(torch, lambda i: gm.gated_mla(x, wts["Wq"], wts["Wc"], wts["Wk"],
                                                               wts["Wv"], wts["Wg"], wts["Wo"],
                                                               ld["H"], True),
-                                max(5, K // 5), 2)
+                                max(5, K // 5), max(2, W // 3))
             T_, dm, dc = ld["T"], ld["d_model"], ld["d_c"]
             lflops = 2 * T_ * (3 * dm * dm + 3 * dm * dc) + prefill_flops(1, T_, ld["H"], dm // ld["H"])
             extra[lw.name] = {"value": round(lflops / (lavg * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
@@ -466,7 +490,8 @@ def main():
             cw = I.WORKLOADS["decode_b4_n131072"]
             cd = cw.dims
             qc, kc, vc, _ = I.workload_inputs(cw.name, dev)
-            cavg, _, _ = time_calls(torch, lambda i: gm.attend_decode(qc, kc, vc), max(5, K // 5), 2)
+            cavg, _, _ = time_calls(torch, lambda i: gm.attend_decode(qc, kc, vc), max(5, K // 5),
+                                    max(2, W // 10))
             cb = decode_bytes(cd["B"], cd["H"], cd["N"], cd["D"])
             extra[cw.name] = {"value": round(cb / (cavg * 1e-3) / 1e9, 1), "unit": "GB/s",
                               "avg_call_ms": round(cavg, 4), "algorithmic_bytes": cb,
