@@ -35,6 +35,34 @@ def test_prefill_b2_t4096_sampled():
         check_rows_rel(got, ref, D)
 
 
+@pytest.mark.parametrize("Tq,Tk", [(16384, 16384), (300, 65536)])
+def test_prefill_long_sampled(Tq, Tk):
+    """Long sequences on the MFMA kernel: a 16384-token causal prefill (the longest of the
+    sequence-length sweep) and a 300-query chunk after 65236 cached tokens (key rows past
+    2^16, an offset off the 64-key tile grid); every output written, sampled rows of two
+    heads against the oracle."""
+    dev = need_gpu()
+    announce(f"prefill long Tq={Tq} Tk={Tk}, sampled rows")
+    H, D = 2, 128
+    out = torch.full((1, Tq, H * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    if Tq == Tk:  # one packed [T, 3, H, D] buffer: q, k and v share their strides
+        qkv = I.normal((1, Tq, 3, H, D), torch.bfloat16, dev, seed=5100 + Tq)
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        gm.attend_prefill(q, k, v, out=out)
+    else:
+        q = I.normal((1, Tq, H, D), torch.bfloat16, dev, seed=5100 + Tq)
+        kv = I.normal((1, Tk, 2, H, D), torch.bfloat16, dev, seed=5101 + Tk)
+        k, v = kv[:, :, 0], kv[:, :, 1]
+        gm.attend_chunk(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "some (head, query block) was never written"
+    rows = sorted(set([0, 1, 63, 64, 127, 128, Tq // 2, Tq - 129, Tq - 2, Tq - 1]))
+    for h in range(H):
+        ref = oracle.attend_head(host(q[0, :, h]), host(k[0, :, h]), host(v[0, :, h]),
+                                 1 / np.sqrt(D), True, rows=rows)
+        check_rows_rel(host(out[0, rows, h * D:(h + 1) * D]), ref, D)
+
+
 def test_decode_b4_n131072_sampled():
     """Decode B=4 H=96 against 131072 keys, split-KV with the log-sum-exp merge:
     sampled heads against the oracle, and the Q = 0 closed form (the mean of all
