@@ -131,7 +131,8 @@ def measure_achievable(torch, dev):
     def mfma(i):
         assert lib.gmla_probe_mfma(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp) == 0
 
-    mavg, _, _ = time_calls(torch, mfma, 5, 2)
+    # ~60 ms of warm-up: the clock the matrix cores hold settles only under sustained load
+    mavg, _, _ = time_calls(torch, mfma, 20, 60)
     nbytes = 2 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     rblocks = 2048
@@ -141,7 +142,7 @@ def measure_achievable(torch, dev):
         assert lib.gmla_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks,
                                    ctypes.c_void_p(rout.data_ptr()), sp) == 0
 
-    ravg, _, _ = time_calls(torch, read, 5, 2)
+    ravg, _, _ = time_calls(torch, read, 10, 10)
     del buf
     return {"mfma_bf16_tflops": round(flops / (mavg * 1e-3) / 1e12, 1),
             "hbm_read_gbps": round(nbytes / (ravg * 1e-3) / 1e9, 1),
