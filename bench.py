@@ -360,10 +360,11 @@ def main():
     # A fresh GPU runs the first few dozen prefill calls up to 30% slower while its clocks
     # settle under sustained matrix-core load; 60 untimed calls reach the steady state.
     ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--all", action="store_true", help="also time the layer and the 131072-key decode")
+    ap.add_argument("--all", action="store_true", help="also time the layer, the 131072-key decode and the latent-cache decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-splits", type=int, default=0)
-    ap.add_argument("--only", choices=["prefill", "decode", "layer", "decode_long", "copy"])
+    ap.add_argument("--only", choices=["prefill", "decode", "layer", "decode_long", "decode_latent",
+                                       "copy"])
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--timed-window", nargs=2, type=int, metavar=("W", "K"),
                     help="with --summarize-stats: also average dispatches W .. W+K-1 per kernel")
@@ -472,7 +473,7 @@ def main():
             result.update({"value": round(gbps, 1), "unit": "GB/s",
                            "ms_per_step": round(dwall * 1e3 / dcalls, 4)})
 
-    if args.all or only in ("layer", "decode_long"):
+    if args.all or only in ("layer", "decode_long", "decode_latent"):
         extra = {}
         if only in (None, "layer"):
             lw = I.WORKLOADS["layer_t2048"]
@@ -498,6 +499,21 @@ def main():
                               "avg_call_ms": round(cavg, 4), "algorithmic_bytes": cb,
                               "splits": gm.decode_num_splits(cd["B"], cd["H"], cd["N"], cd["D"])}
             del qc, kc, vc
+        if only in (None, "decode_latent"):
+            # decode over the latent cache at the 1001-key shape: C [8, 1001, 512] is the
+            # whole cache; K and V are rebuilt from it by the latent expansion every call
+            B_, N_, H_, D_, dc = 8, 1001, 96, 128, 512
+            ql = I.normal((B_, H_, D_), torch.bfloat16, dev, seed=7001)
+            cl = I.normal((B_, N_, dc), torch.bfloat16, dev, seed=7002)
+            wkl = I.normal((H_ * D_, dc), torch.bfloat16, dev, seed=7003, std=dc ** -0.5)
+            wvl = I.normal((H_ * D_, dc), torch.bfloat16, dev, seed=7004, std=dc ** -0.5)
+            lavg2, _, _ = time_calls(torch, lambda i: gm.attend_decode_latent(ql, cl, wkl, wvl),
+                                     max(5, K // 5), max(2, W // 10))
+            extra["decode_latent_b8_n1001"] = {
+                "value": round(lavg2, 4), "unit": "ms per call", "cache_bytes": B_ * N_ * dc * 2,
+                "expansion_flop": 2 * B_ * N_ * dc * H_ * D_ * 2,
+                "note": "K and V rebuilt from the 512-wide latent cache by one GEMM launch, then decode"}
+            del ql, cl, wkl, wvl
         result["extra"] = extra
 
     if not args.no_cpu and only is None:

@@ -28,7 +28,8 @@ import torch
 from . import _lib
 from ._lib import GMLA_BF16, GMLA_F32, GmlaError, LIB_PATH  # noqa: F401
 
-__all__ = ["attend_prefill", "attend_chunk", "attend_decode", "latent_expand", "gate_out", "linear", "gated_mla",
+__all__ = ["attend_prefill", "attend_chunk", "attend_decode", "attend_decode_latent", "latent_expand", "gate_out",
+           "linear", "gated_mla",
            "decode_num_splits", "decode_workspace_bytes", "library", "GmlaError"]
 
 _DTYPES = {torch.float32: GMLA_F32, torch.bfloat16: GMLA_BF16}
@@ -201,6 +202,35 @@ def attend_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch
                                 int(num_splits), _stream(dev, stream))
     _lib.check(st, "gmla_attend_decode")
     return out
+
+
+def attend_decode_latent(q: torch.Tensor, latent_cache: torch.Tensor, key_up_projection: torch.Tensor,
+                         value_up_projection: torch.Tensor, gate: torch.Tensor | None = None, *,
+                         scale: float | None = None, num_splits: int = 0, out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """Decode over the latent cache: the cache holds only C [B, N, d_c] and the keys and
+    values are rebuilt from it when attention runs ("Gated MLA", "Start from familiar
+    attention": K = C W_k^T, V = C W_v^T; "Le Transformer et l'attention", "MLA —
+    compresser en un vecteur latent"), then one query per head at position N-1 attends
+    to all N of them.
+
+    q: [B, H, D] contiguous; latent_cache: [B, N, d_c] contiguous; key/value up-projections
+    [H*D, d_c].  Two library calls: the latent expansion of the N cached tokens
+    (2 * B * N * d_c * H * D * 2 flop) into [B, N, H*D] buffers, then the decode kernel on
+    [B, H, N, D] views of them.  Returns [B, H*D].
+    """
+    if q.dim() != 3 or latent_cache.dim() != 3:
+        raise ValueError("q must be [B, H, D] and latent_cache [B, N, d_c]")
+    B, H, D = q.shape
+    if latent_cache.shape[0] != B:
+        raise ValueError("q and latent_cache disagree on the batch size")
+    N = latent_cache.shape[1]
+    if key_up_projection.shape[0] != H * D:
+        raise ValueError("the up-projections must have H*D rows")
+    k_full, v_full = latent_expand(latent_cache, key_up_projection, value_up_projection, stream=stream)
+    k = k_full.view(B, N, H, D).permute(0, 2, 1, 3)  # [B, H, N, D], strides (b, h, n)
+    v = v_full.view(B, N, H, D).permute(0, 2, 1, 3)
+    return attend_decode(q, k, v, gate, scale=scale, num_splits=num_splits, out=out, stream=stream)
 
 
 def latent_expand(c: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, *, stream=None):

@@ -202,6 +202,35 @@ def test_decode_b8_n1001(splits):
     check_rows_rel(host(out), ref, D)
 
 
+@pytest.mark.parametrize("B,N,H,dc,gate", [(2, 300, 4, 64, True), (8, 1001, 96, 512, False)])
+def test_decode_latent_cache(B, N, H, dc, gate):
+    """Decode over the latent cache (K, V rebuilt from C when attention runs), against the
+    oracle's composition: K_h = C W_k,h^T, V_h = C W_v,h^T in double, then the softmax of
+    the last position over all N keys; every head at the small shape, sampled heads at
+    the pages' decode shape (B=8, H=96, 1001 keys, 512-wide latent)."""
+    dev = need_gpu()
+    D = 128
+    announce(f"decode over latent cache B={B} N={N} H={H} d_c={dc}")
+    q = I.normal((B, H, D), torch.bfloat16, dev, seed=3300 + N)
+    c = I.normal((B, N, dc), torch.bfloat16, dev, seed=3301 + N)
+    wk = I.normal((H * D, dc), torch.bfloat16, dev, seed=3302 + N, std=dc ** -0.5)
+    wv = I.normal((H * D, dc), torch.bfloat16, dev, seed=3303 + N, std=dc ** -0.5)
+    g = I.normal((B, H * D), torch.bfloat16, dev, seed=3304 + N) if gate else None
+    out = gm.attend_decode_latent(q, c, wk, wv, g)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(N)
+    pairs = ([(b, h) for b in range(B) for h in range(H)] if B * H <= 16 else
+             [(0, 0), (B - 1, H - 1)] + [(int(r.integers(B)), int(r.integers(H))) for _ in range(6)])
+    hc, hq, hwk, hwv = host(c), host(q), host(wk), host(wv)
+    for b, h in pairs:
+        kh = oracle.linear(hc[b], hwk[h * D:(h + 1) * D])
+        vh = oracle.linear(hc[b], hwv[h * D:(h + 1) * D])
+        ref = oracle.attend_head(hq[b, h][None, :], kh, vh, 1 / np.sqrt(D), True)
+        if gate:
+            ref = oracle.gate(host(g)[b, h * D:(h + 1) * D][None, :], ref)
+        check_rows_rel(host(out)[b, h * D:(h + 1) * D][None, :], ref, D)
+
+
 @pytest.mark.parametrize("N", [1, 2, 17, 64, 255, 256, 257, 1000])
 @pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (128, torch.float32),
                                      (64, torch.bfloat16), (32, torch.float32)])
