@@ -168,6 +168,18 @@ def test_binding_rejects_cpu_tensors_and_mismatches():
         gm.gated_mla(x, *([torch.zeros(6, 6)] * 6), num_heads=4)
     with pytest.raises(TypeError):
         gm.gated_mla(x, *([torch.zeros(6, 6)] * 6), num_heads=2, causal="yes")
+    # decode over the latent cache: shape checks come before any device work
+    qd = torch.zeros(2, 4, 128, dtype=torch.bfloat16)
+    c = torch.zeros(2, 10, 64, dtype=torch.bfloat16)
+    w = torch.zeros(4 * 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gm.attend_decode_latent(qd[0], c, w, w)            # q not [B, H, D]
+    with pytest.raises(ValueError):
+        gm.attend_decode_latent(qd, c[:1], w, w)           # batch sizes differ
+    with pytest.raises(ValueError):
+        gm.attend_decode_latent(qd, c, w[:256], w[:256])   # up-projections not H*D rows
+    with pytest.raises(ValueError):
+        gm.attend_decode_latent(qd, c, w, w)               # host tensors
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
