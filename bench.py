@@ -13,8 +13,10 @@ compares the dominant kernel with MI355X's published peaks; ``cpu_baseline`` tim
 the plain CPU oracle on a bounded sample of the same workload.
 
 Profiling helpers (no compute of their own):
-    python bench.py --only prefill|decode|layer|decode_long|copy --steps K
+    python bench.py --only prefill|decode|layer|decode_long|decode_latent|copy --steps K
         run just that part, for rocprofv3 --kernel-trace or --pmc passes;
+    python bench.py --only prefill --loop SECONDS
+        call the prefill back to back (to sample clocks with rocm-smi meanwhile);
     python bench.py --summarize-stats DIR --name NAME --cmd "..."
     python bench.py --summarize-mfma DIR --name NAME --cmd "..."
         turn rocprofv3 kernel statistics in DIR into profiles/NAME.md;
@@ -110,6 +112,24 @@ def time_calls(torch, fn, steps, warmup, rotate=1):
         torch.cuda.synchronize()
         fastest = min(fastest, e0.elapsed_time(e1) / 10)
     return region / steps, fastest, wall
+
+
+def loop_calls(torch, fn, seconds, work, unit):
+    """Call fn back to back for about `seconds`, printing the rate of each 20-call batch
+    every half second (for sampling clocks or power from another process meanwhile)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = last = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        e0.record()
+        for i in range(20):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        if time.perf_counter() - last > 0.5:
+            last = time.perf_counter()
+            rate = work * 20 / (e0.elapsed_time(e1) * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+            print(json.dumps({"t": round(last - t0, 2), "value": round(rate, 1), "unit": unit}),
+                  flush=True)
 
 
 def measure_achievable(torch, dev):
@@ -371,6 +391,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--loop", type=float, metavar="SECONDS",
+                    help="with --only prefill: call it back to back for SECONDS, printing rates")
     ap.add_argument("--name")
     ap.add_argument("--kernel")
     ap.add_argument("--key", help="record name in traffic.json (default: the kernel)")
@@ -423,6 +445,9 @@ def main():
         q, k, v, _ = I.workload_inputs(pw.name, dev)
         out = torch.empty((d["B"], d["T"], d["H"] * d["D"]), dtype=q.dtype, device=dev)
         flops = prefill_flops(d["B"], d["T"], d["H"], d["D"])
+        if args.loop:
+            return loop_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), args.loop,
+                              flops, "TFLOP/s")
         avg, fastest, wall = time_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), K, W)
         tflops = flops / (avg * 1e-3) / 1e12
         result.update({
