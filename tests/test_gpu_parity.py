@@ -333,13 +333,13 @@ def test_linear_mid_ragged(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2000, 12200, 320), (2048, 12296, 1024), (1999, 12288, 1088),
-                                   (2048, 12288, 1024)])
+                                   (2048, 12288, 1024), (3, 98304, 1024)])
 def test_linear_large_tiles_ragged(M, N, K):
     """Products with enough large tiles to fill the CUs: 256 x 192 tiles (the first two: N
     not a multiple of 192, or K deep but N not a multiple of 384) and 256 x 384 tiles (K >=
-    1024 and N a multiple of 384; M not a multiple of 256, and an odd number of 64-deep
-    stages).  The output starts as NaN: every element is written; sampled rows match the
-    oracle across the full width."""
+    1024 and N a multiple of 384; M not a multiple of 256, an odd number of 64-deep
+    stages, and three rows in 256-row tiles).  The output starts as NaN: every element is
+    written; sampled rows match the oracle across the full width."""
     dev = need_gpu()
     announce(f"linear large tiles {M}x{N}x{K}")
     x = I.normal((M, K), torch.bfloat16, dev, seed=4400 + K)
@@ -348,7 +348,8 @@ def test_linear_large_tiles_ragged(M, N, K):
     gm.linear(x, w, out=y)
     torch.cuda.synchronize()
     assert not torch.isnan(y).any()
-    rows = sorted(set(list(range(0, M, 89)) + [M - 1, M - 2, 255, 256, 1791, 1792]))
+    rows = sorted(r for r in set(list(range(0, M, 89)) + [M - 1, M - 2, 255, 256, 1791, 1792])
+                  if 0 <= r < M)
     check_rows_rel(host(y)[rows], oracle.linear(host(x)[rows], host(w)), N)
 
 
