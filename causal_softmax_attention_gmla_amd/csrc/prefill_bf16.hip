@@ -371,9 +371,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     };
 
     if constexpr (NEXT == 2) {
-      // last tile: weights, then values
-      static_for<16>([&](auto U) { eunit(U); });
-      static_for<16>([&](auto I) { pv_mfma(I, vread(I)); });
+      // last tile: weights, then values.  A 32-key half past every key this wave's
+      // queries may see holds only masked scores (weight exactly 0): its exponentials and
+      // value MFMAs would add zeros, so the wave skips them.
+      const int wlim = a.causal ? min(wq0 + 31 + off, Tk - 1) : Tk - 1;
+      const bool live0 = j * BN <= wlim, live1 = j * BN + 32 <= wlim;
+      if (live0) {
+        static_for<8>([&](auto U) { eunit(U); });
+        static_for<8>([&](auto I) { pv_mfma(I, vread(I)); });
+      }
+      if (live1) {
+        static_for<8>([&](auto U) { eunit(std::integral_constant<int, decltype(U)::value + 8>{}); });
+        static_for<8>([&](auto I) {
+          constexpr int i = decltype(I)::value + 8;
+          pv_mfma(std::integral_constant<int, i>{}, vread(std::integral_constant<int, i>{}));
+        });
+      }
     } else {
       f32x16 s_next[2];
       s_next[0] = f32x16{};
