@@ -42,9 +42,12 @@
 //  * The queries may be the last T rows of Tk >= T keys (a chunk after a cache):
 //    query i sits at position i + Tk - T and sees the keys up to there ("Kimi K2 -
 //    Construct causal mask": positions continue from the cached length).
+//  * On a block's last tile a wave skips the 32-key halves that none of its queries may
+//    see (their weights are exactly 0).
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
-//    (shared L2); an XCD's heads go in groups of four whose query blocks launch
-//    heaviest (longest prefix) first across the group.
+//    (shared L2); an XCD's heads go in groups of four (one group when the XCD has at
+//    most three blocks per workgroup slot) whose query blocks launch heaviest (longest
+//    prefix) first across the group.
 #include <type_traits>
 #include <utility>
 
