@@ -44,7 +44,7 @@ typedef enum { GMLA_F32 = 0, GMLA_BF16 = 1 } gmla_dtype;
 typedef enum {
   GMLA_OK = 0,
   GMLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad flag, misaligned pointer */
-  GMLA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype this build has no kernel for */
+  GMLA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype the library has no kernel for */
   GMLA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
   GMLA_ERR_HIP = -4          /* the HIP runtime reported an error (no device, launch failure) */
 } gmla_status;
