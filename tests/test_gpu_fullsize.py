@@ -63,6 +63,28 @@ def test_prefill_long_sampled(Tq, Tk):
         check_rows_rel(host(out[0, rows, h * D:(h + 1) * D]), ref, D)
 
 
+def test_prefill_offsets_past_2_31_sampled():
+    """Causal prefill B=2 T=65536 H=96 from one packed [B, T, 3, H, D] buffer: the second
+    batch's rows start 2.4e9 elements in, past 32-bit element offsets; every output
+    written, sampled rows of heads in both batches against the oracle."""
+    dev = need_gpu()
+    B, T, H, D = 2, 65536, 96, 128
+    announce(f"prefill B={B} T={T} H={H}: element offsets past 2^31")
+    qkv = I.normal((B * T, 3, H, D), torch.bfloat16, dev, seed=5200).view(B, T, 3, H, D)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    assert q.stride(0) * (B - 1) > 2 ** 31
+    out = torch.full((B, T, H * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.attend_prefill(q, k, v, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any(), "some (head, query block) was never written"
+    rows = [0, 127, 128, 40000, T - 1]
+    for b, h in [(0, 5), (1, 0), (1, H - 1)]:
+        ref = oracle.attend_head(host(q[b, :, h]), host(k[b, :, h]), host(v[b, :, h]),
+                                 1 / np.sqrt(D), True, rows=rows)
+        check_rows_rel(host(out[b, rows, h * D:(h + 1) * D]), ref, D)
+    del qkv, out
+
+
 def test_decode_b4_n131072_sampled():
     """Decode B=4 H=96 against 131072 keys, split-KV with the log-sum-exp merge:
     sampled heads against the oracle, and the Q = 0 closed form (the mean of all
