@@ -85,6 +85,24 @@ def test_prefill_offsets_past_2_31_sampled():
     del qkv, out
 
 
+def test_linear_offsets_past_2_31_sampled():
+    """Y = X W^T with X [300000, 8192] (2.46e9 elements, past 32-bit element offsets) on
+    the 256 x 384-tile kernel; every output written, sampled rows (the last ones beyond
+    2^31 elements into X) against the oracle."""
+    dev = need_gpu()
+    M, N, K = 300000, 384, 8192
+    announce(f"linear {M}x{N}x{K}: element offsets past 2^31")
+    x = I.normal((M, K), torch.bfloat16, dev, seed=5300)
+    w = I.normal((N, K), torch.bfloat16, dev, seed=5301, std=K ** -0.5)
+    y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.linear(x, w, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    rows = [0, 255, 256, 262143, 262144, 299999]
+    check_rows_rel(host(y[rows]), oracle.linear(host(x[rows]), host(w)), N)
+    del x, y
+
+
 def test_decode_b4_n131072_sampled():
     """Decode B=4 H=96 against 131072 keys, split-KV with the log-sum-exp merge:
     sampled heads against the oracle, and the Q = 0 closed form (the mean of all
