@@ -7,7 +7,10 @@ the library; every arithmetic step runs in the library's HIP kernels.
 
     attend_prefill(q, k, v, gate=None, scale=None, causal=True)   -> [B, T, H*D]
     attend_chunk(q, k, v, gate=None, scale=None, causal=True)     -> [B, Tq, H*D]
+    attend_varlen(q, k, v, cu_q, cu_k, max_q, max_k, gate=None)   -> [total_q, H*D]
     attend_decode(q, k, v, gate=None, scale=None, num_splits=0)   -> [B, H*D]
+    attend_decode_varlen(q, k, v, kv_lens, gate=None)             -> [B, H*D]
+    attend_decode_latent(q, c, w_k, w_v, gate=None)               -> [B, H*D]
     latent_expand(c, w_k, w_v)                                    -> (K, V)
     gate_out(o_tilde, w_o=None, gate=None)                        -> Y
     linear(x, w)                                                  -> x w^T
@@ -28,9 +31,10 @@ import torch
 from . import _lib
 from ._lib import GMLA_BF16, GMLA_F32, GmlaError, LIB_PATH  # noqa: F401
 
-__all__ = ["attend_prefill", "attend_chunk", "attend_decode", "attend_decode_latent", "latent_expand", "gate_out",
-           "linear", "gated_mla",
-           "decode_num_splits", "decode_workspace_bytes", "library", "GmlaError"]
+__all__ = ["attend_prefill", "attend_chunk", "attend_varlen", "attend_decode", "attend_decode_varlen",
+           "attend_decode_latent", "latent_expand", "gate_out",
+           "linear", "gated_mla", "decode_num_splits", "decode_workspace_bytes",
+           "decode_latent_num_splits", "decode_latent_workspace_bytes", "library", "GmlaError"]
 
 _DTYPES = {torch.float32: GMLA_F32, torch.bfloat16: GMLA_BF16}
 
@@ -157,6 +161,62 @@ def attend_chunk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.
     return out
 
 
+def attend_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int | None = None,
+                  max_seqlen_k: int | None = None, gate: torch.Tensor | None = None, *,
+                  scale: float | None = None, causal: bool = True, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """Attention over a packed batch of sequences of different lengths: sequence b owns
+    query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1]-1, and its query i sits at position i + Tk_b - Tq_b (bottom-right
+    causal mask per sequence).  A query that sees no key gets zeros.
+
+    q: [total_q, H, D]; k, v: [total_k, H, D] with identical strides; every last axis
+    contiguous.  cu_seqlens_*: int32 device tensors [B + 1].  max_seqlen_q / _k: the
+    longest sequences (read back from the offsets, a host sync, when omitted).  gate:
+    optional [total_q, H*D].  Returns [total_q, H*D].
+    """
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [total_q, H, D] and k, v [total_k, H, D]")
+    total_q, H, D = q.shape
+    if (k.shape[1], k.shape[2]) != (H, D):
+        raise ValueError("q and k, v disagree in heads or head width")
+    if k.stride() != v.stride() or k.stride(2) != 1 or q.stride(2) != 1:
+        raise ValueError("k, v need identical strides; every last axis must be contiguous")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors")
+    B = cu_seqlens_q.numel() - 1
+    if B < 1 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
+    if not isinstance(causal, bool):
+        raise TypeError("causal must be a bool")
+    dev = _dev(q, k, v, cu_seqlens_q, cu_seqlens_k, gate, out)
+    _same_dtype(q, k, v, gate, out)
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item())
+    if max_seqlen_k is None:
+        max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item())
+    if gate is not None and (gate.shape != (total_q, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [total_q, H*D] tensor")
+    if out is None:
+        out = torch.empty((total_q, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (total_q, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [total_q, H*D] tensor")
+    if max_seqlen_q == 0:
+        return out
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qs = (ctypes.c_int64 * 2)(q.stride(0), q.stride(1))
+    kvs = (ctypes.c_int64 * 2)(k.stride(0), k.stride(1))
+    st = _lib.load().gmla_attend_varlen(_dtype(q), B, H, D, float(scale), int(causal), _ptr(q), qs,
+                                        _ptr(cu_seqlens_q), int(max_seqlen_q), _ptr(k), _ptr(v), kvs,
+                                        _ptr(cu_seqlens_k), int(max_seqlen_k), _ptr(gate), _ptr(out),
+                                        _stream(dev, stream))
+    _lib.check(st, "gmla_attend_varlen")
+    return out
+
+
 def decode_num_splits(B: int, H: int, N: int, D: int) -> int:
     return _lib.load().gmla_decode_num_splits(B, H, N, D)
 
@@ -204,33 +264,106 @@ def attend_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch
     return out
 
 
+def attend_decode_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_lens: torch.Tensor,
+                         gate: torch.Tensor | None = None, *, scale: float | None = None,
+                         num_splits: int = 0, workspace: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode with a cache length per batch row: row b's query sits at position
+    kv_lens[b] - 1 and attends to keys 0 .. kv_lens[b] - 1 of its cache (values clamped to
+    [0, N]; an empty row gives zeros).  q: [B, H, D]; k, v: [B, H, N, D] caches of
+    capacity N; kv_lens: int32 device tensor [B].  Returns [B, H*D]."""
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, D] and k, v [B, H, N, D]")
+    B, H, N, D = k.shape
+    if q.shape != (B, H, D) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, D] tensor")
+    if k.stride() != v.stride() or k.stride(3) != 1:
+        raise ValueError("k, v need identical strides and a contiguous last axis")
+    if kv_lens.dtype != torch.int32 or kv_lens.shape != (B,) or not kv_lens.is_contiguous():
+        raise ValueError("kv_lens must be a contiguous int32 tensor [B]")
+    dev = _dev(q, k, v, kv_lens, gate, out, workspace)
+    _same_dtype(q, k, v, gate, out)
+    if gate is not None and (gate.shape != (B, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [B, H*D] tensor")
+    if out is None:
+        out = torch.empty((B, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H*D] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    need = lib.gmla_decode_workspace_bytes(B, H, N, D, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    strides = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    st = lib.gmla_attend_decode_varlen(_dtype(q), B, H, N, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                       strides, _ptr(kv_lens), _ptr(gate), _ptr(out), _ptr(workspace),
+                                       ws_bytes, int(num_splits), _stream(dev, stream))
+    _lib.check(st, "gmla_attend_decode_varlen")
+    return out
+
+
+def decode_latent_num_splits(B: int, H: int, N: int, d_c: int) -> int:
+    return _lib.load().gmla_decode_latent_num_splits(B, H, N, d_c)
+
+
+def decode_latent_workspace_bytes(B: int, H: int, N: int, d_c: int, num_splits: int = 0) -> int:
+    return _lib.load().gmla_decode_latent_workspace_bytes(B, H, N, d_c, num_splits)
+
+
 def attend_decode_latent(q: torch.Tensor, latent_cache: torch.Tensor, key_up_projection: torch.Tensor,
                          value_up_projection: torch.Tensor, gate: torch.Tensor | None = None, *,
-                         scale: float | None = None, num_splits: int = 0, out: torch.Tensor | None = None,
+                         scale: float | None = None, num_splits: int = 0,
+                         workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                          stream=None) -> torch.Tensor:
-    """Decode over the latent cache: the cache holds only C [B, N, d_c] and the keys and
-    values are rebuilt from it when attention runs ("Gated MLA", "Start from familiar
-    attention": K = C W_k^T, V = C W_v^T; "Le Transformer et l'attention", "MLA —
-    compresser en un vecteur latent"), then one query per head at position N-1 attends
-    to all N of them.
+    """Decode over the latent cache: the cache holds only C [B, N, d_c]; the keys and values
+    K_h = C W_k,h^T, V_h = C W_v,h^T are never formed ("Gated MLA", "Start from familiar
+    attention" and "Common mistakes to avoid"; "Le Transformer et l'attention", "MLA —
+    compresser en un vecteur latent").  One query per head at position N-1 attends to all
+    N cached tokens; the library regroups the products exactly (scores against
+    W_k,h^T q_h, values as W_v,h times the weighted latent sum).
 
-    q: [B, H, D] contiguous; latent_cache: [B, N, d_c] contiguous; key/value up-projections
-    [H*D, d_c].  Two library calls: the latent expansion of the N cached tokens
-    (2 * B * N * d_c * H * D * 2 flop) into [B, N, H*D] buffers, then the decode kernel on
-    [B, H, N, D] views of them.  Returns [B, H*D].
+    q: [B, H, D] contiguous; latent_cache: [B, N, d_c] with a contiguous last axis (row
+    strides free); key/value up-projections [H*D, d_c] contiguous; gate: optional
+    [B, H*D].  Returns [B, H*D].
     """
     if q.dim() != 3 or latent_cache.dim() != 3:
         raise ValueError("q must be [B, H, D] and latent_cache [B, N, d_c]")
     B, H, D = q.shape
     if latent_cache.shape[0] != B:
         raise ValueError("q and latent_cache disagree on the batch size")
-    N = latent_cache.shape[1]
-    if key_up_projection.shape[0] != H * D:
-        raise ValueError("the up-projections must have H*D rows")
-    k_full, v_full = latent_expand(latent_cache, key_up_projection, value_up_projection, stream=stream)
-    k = k_full.view(B, N, H, D).permute(0, 2, 1, 3)  # [B, H, N, D], strides (b, h, n)
-    v = v_full.view(B, N, H, D).permute(0, 2, 1, 3)
-    return attend_decode(q, k, v, gate, scale=scale, num_splits=num_splits, out=out, stream=stream)
+    N, d_c = latent_cache.shape[1], latent_cache.shape[2]
+    for w in (key_up_projection, value_up_projection):
+        if w.shape != (H * D, d_c):
+            raise ValueError("the up-projections must be [H*D, d_c]")
+        if not w.is_contiguous():
+            raise ValueError("the up-projections must be contiguous")
+    if not q.is_contiguous() or latent_cache.stride(2) != 1:
+        raise ValueError("q must be contiguous and the latent cache rows contiguous")
+    dev = _dev(q, latent_cache, key_up_projection, value_up_projection, gate, out, workspace)
+    _same_dtype(q, latent_cache, key_up_projection, value_up_projection, gate, out)
+    if gate is not None and (gate.shape != (B, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [B, H*D] tensor")
+    if out is None:
+        out = torch.empty((B, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H*D] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    need = lib.gmla_decode_latent_workspace_bytes(B, H, N, d_c, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    strides = (ctypes.c_int64 * 2)(latent_cache.stride(0), latent_cache.stride(1))
+    st = lib.gmla_attend_decode_latent(_dtype(q), B, H, N, D, d_c, float(scale), _ptr(q),
+                                       _ptr(latent_cache), strides, _ptr(key_up_projection),
+                                       _ptr(value_up_projection), _ptr(gate), _ptr(out),
+                                       _ptr(workspace), ws_bytes, int(num_splits),
+                                       _stream(dev, stream))
+    _lib.check(st, "gmla_attend_decode_latent")
+    return out
 
 
 def latent_expand(c: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, *, stream=None):

@@ -29,10 +29,18 @@ SIGNATURES = {
     "gmla_attend_prefill": (_i, [_i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _i64p, _vp, _vp, _vp]),
     "gmla_attend_chunk": (_i, [_i, _i, _i, _i, _i, _i, _f, _i, _vp, _i64p, _vp, _vp, _i64p, _vp,
                                _vp, _vp]),
+    "gmla_attend_varlen": (_i, [_i, _i, _i, _i, _f, _i, _vp, _i64p, _vp, _i, _vp, _vp, _i64p, _vp,
+                                _i, _vp, _vp, _vp]),
+    "gmla_attend_decode_varlen": (_i, [_i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _i64p, _vp, _vp, _vp,
+                                       _vp, ctypes.c_size_t, _i, _vp]),
     "gmla_decode_num_splits": (_i, [_i, _i, _i, _i]),
     "gmla_decode_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "gmla_attend_decode": (_i, [_i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _i64p, _vp, _vp, _vp,
                                 ctypes.c_size_t, _i, _vp]),
+    "gmla_decode_latent_num_splits": (_i, [_i, _i, _i, _i]),
+    "gmla_decode_latent_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
+    "gmla_attend_decode_latent": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i64p, _vp, _vp, _vp,
+                                       _vp, _vp, ctypes.c_size_t, _i, _vp]),
     "gmla_latent_expand": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gmla_gate_out": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "gmla_linear": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp]),

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libgmla.so")
 PROBE_LIB = os.path.join(HERE, "libgmla_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["gmla_api.hip", "prefill_bf16.hip", "prefill_simple.hip", "decode.hip", "gemm.hip", "gemm_lds.hip"]
+SOURCES = ["gmla_api.hip", "prefill_bf16.hip", "prefill_simple.hip", "decode.hip", "decode_latent.hip", "gemm.hip", "gemm_lds.hip"]
 # measurement aids for the benchmark, linked into their own library
 PROBE_SOURCES = ["probe.hip"]
 

@@ -18,6 +18,9 @@
 //    by log-sum-exp: m = max_j m_j, l = sum_j l_j 2^(m_j - m),
 //    o = sum_j o_j 2^(m_j - m) / l -- an exact regrouping of the one softmax over all
 //    keys ("Kimi K3 - Softmax over keys", the formula).
+//  * Per-row cache lengths (an optional device array): row b holds its own number of
+//    keys, and its query sits at position lens[b] - 1; the key ranges are those of the
+//    longest row, so a shorter row's later ranges are empty (m = -inf, weight 0).
 //  * With one split the workgroup writes the final (normalised, optionally gated)
 //    output itself; otherwise it writes (m, l, o) to the workspace and a small merge
 //    kernel finishes.
@@ -97,7 +100,7 @@ __device__ __forceinline__ Partial shfl_partial(const Partial& p, int mask) {
   return r;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool LENS>
 __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, int keys_per_split) {
   constexpr int LPK = D / 8;      // lanes per key row
   constexpr int KPW = 64 / LPK;   // key rows per wave per load
@@ -110,8 +113,11 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, int keys
   const int c8 = lane % LPK;  // channel chunk: channels 8*c8 .. 8*c8+7
   const int kr = lane / LPK;  // key row within a load
 
+  // with per-row cache lengths, row b holds lens[b] keys (clamped to [0, N]) and its query
+  // sits at position lens[b] - 1
+  const int nb = LENS ? min(max(a.lens[b], 0), a.N) : a.N;
   const int n0 = split * keys_per_split;
-  const int n1 = min(a.N, n0 + keys_per_split);
+  const int n1 = min(nb, n0 + keys_per_split);
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const T* Kh = (const T*)a.k + head_off + c8 * 8;
   const T* Vh = (const T*)a.v + head_off + c8 * 8;
@@ -182,7 +188,8 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, int keys
 
   if (a.splits == 1) {
     const int64_t row = ((int64_t)b * a.H + h) * D + c8 * 8;
-    const float inv = 1.0f / tot.l;
+    // (an empty cache row, possible only with per-row lengths, gives zeros)
+    const float inv = (LENS && tot.l == 0.0f) ? 0.0f : 1.0f / tot.l;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = tot.o[e] * inv;
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(NT) void decode_split_kernel(DecodeArgs a, int keys
 }
 
 // One workgroup per (batch, head), one lane per channel.
-template <typename T, int D>
+template <typename T, int D, bool LENS>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const float* ws = a.ws + ((int64_t)b * a.H + h) * a.splits * (D + 2);
@@ -216,20 +223,25 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     o = __builtin_fmaf(ws[j * (D + 2) + 2 + d], f, o);
   }
   const int64_t idx = ((int64_t)b * a.H + h) * D + d;
-  float v = o / l;
+  float v = (LENS && l == 0.0f) ? 0.0f : o / l;
   if (a.g) v *= sigmoidf_(Elem<T>::load((const T*)a.g + idx));
   Elem<T>::store((T*)a.o + idx, v);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool LENS>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const int kps = (a.N + a.splits - 1) / a.splits;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.splits, a.H, a.B), dim3(NT), 0, s, a,
-                     kps);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, LENS>), dim3(a.splits, a.H, a.B), dim3(NT), 0, s,
+                     a, kps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.H, a.B), dim3(D), 0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, LENS>), dim3(a.H, a.B), dim3(D), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_decode_l(const DecodeArgs& a, hipStream_t s) {
+  return a.lens ? launch_decode_t<T, D, true>(a, s) : launch_decode_t<T, D, false>(a, s);
 }
 
 }  // namespace
@@ -237,9 +249,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
   const bool bf = dtype == 1;
   switch (a.D) {
-    case 32: return bf ? launch_decode_t<bf16, 32>(a, s) : launch_decode_t<float, 32>(a, s);
-    case 64: return bf ? launch_decode_t<bf16, 64>(a, s) : launch_decode_t<float, 64>(a, s);
-    case 128: return bf ? launch_decode_t<bf16, 128>(a, s) : launch_decode_t<float, 128>(a, s);
+    case 32: return bf ? launch_decode_l<bf16, 32>(a, s) : launch_decode_l<float, 32>(a, s);
+    case 64: return bf ? launch_decode_l<bf16, 64>(a, s) : launch_decode_l<float, 64>(a, s);
+    case 128: return bf ? launch_decode_l<bf16, 128>(a, s) : launch_decode_l<float, 128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,415 @@
+// Decode over the latent cache: one new query per (batch, head) against N cached tokens
+// whose keys and values exist only as the latent rows c_n of width d_c ("Gated MLA",
+// section "Start from familiar attention": K = C W_k^T, V = C W_v^T, and "Common mistakes
+// to avoid": the cache is the compact latent tensor, not reconstructed keys and values;
+// "Le Transformer et l'attention", "MLA - compresser en un vecteur latent": 512 cached
+// values per token against 96 x 256 for full keys and values).  The query sits at
+// position N - 1 and sees every cached token ("Kimi K3 - Softmax over keys").
+//
+// The keys and values are never formed.  With W_k,h and W_v,h the 128 rows of W_k and
+// W_v that belong to head h, the products regroup exactly:
+//     s_n = scale * q_h . (W_k,h c_n) = (scale * W_k,h^T q_h) . c_n = q'_h . c_n
+//     o_h = sum_n p_n (W_v,h c_n)     = W_v,h (sum_n p_n c_n)      = W_v,h u_h
+// so every head attends directly over the shared latent rows, and the per-token bytes
+// read are the d_c latent values (shared by all heads) instead of H * 256 key and value
+// values.  Three launches:
+//  1. absorb:  q'[b, h, :] = scale * log2(e) * W_k,h^T q[b, h, :]  (bf16, workspace);
+//  2. split:   grid (split, 32-head block, batch).  The workgroup's key range is walked
+//     in tiles of 32 latent rows staged in LDS (buffer loads in the LDS-direct form, one
+//     tile ahead; rows past N load as zeros).  Wave w owns latent channels
+//     [w d_c / 4, (w + 1) d_c / 4): it forms its share of the scores S^T = C q'^T
+//     (v_mfma_f32_32x32x16_bf16, keys x heads), the four shares are summed through LDS in
+//     a fixed order (every wave then holds the same scores), the online softmax runs in
+//     base 2 per head, and the wave accumulates its channels of U^T = C^T P^T, reading
+//     the tile transposed with ds_read_b64_tr_b16 so that the weights never move between
+//     lanes.  Each split writes (m, l, u[d_c]) per head.
+//  3. merge:   per (head, 32 output channels), for every batch row: the log-sum-exp merge
+//     of the splits (an exact regrouping of the one softmax), u / l, then
+//     o = W_v,h u, the optional sigmoid gate ("Gated MLA", section "The channel-wise
+//     output gate"), and the bf16 store into [B, H*128].
+#include <type_traits>
+
+#include "gmla_internal.h"
+
+namespace gmla {
+namespace {
+
+constexpr int LHD = 128;          // head width
+constexpr int HB = 32;            // heads per split workgroup
+constexpr int KT = 32;            // latent rows per tile
+constexpr int NT = 256;           // 4 waves
+constexpr int kMaxDc = 512;
+constexpr float kLazyRescale = 8.0f;  // raise the running max only past 2^8 growth
+constexpr int kBufferDword3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// One array per buffer, so the compiler can tell a load into one from reads of the other.
+__shared__ __align__(16) bf16 lat_c0[KT * kMaxDc];
+__shared__ __align__(16) bf16 lat_c1[KT * kMaxDc];
+__shared__ __align__(16) f32x4 lat_x0[4 * 4 * 64];  // score shares [wave][quad][lane]
+__shared__ __align__(16) f32x4 lat_x1[4 * 4 * 64];
+template <int P> __device__ __forceinline__ bf16* cbuf() { return P ? lat_c1 : lat_c0; }
+template <int P> __device__ __forceinline__ f32x4* xbuf() { return P ? lat_x1 : lat_x0; }
+
+// Swizzle of the 16-byte chunk index inside each group of 16 chunks of a tile row.  The
+// score reads take one chunk of 32 consecutive rows; the transposing reads take four
+// chunks of rows 4i .. 4i+3: rows 0..3 XOR bits 2-3 and consecutive rows differ in the
+// low bits, so both kinds spread over distinct banks.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int phys_chunk(int row, int c) { return (c & ~15) | ((c & 15) ^ swz(row)); }
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int... Is, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// ---------------------------------------------------------------- 1. absorb W_k into q
+// grid (d_c / 64, H); thread t: latent channel 64 blockIdx.x + t mod 64, head channels
+// [32 (t / 64), 32 (t / 64) + 32).
+template <int DC>
+__global__ __launch_bounds__(NT) void latent_absorb_kernel(LatentDecodeArgs a) {
+  __shared__ float red[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, dg = tid >> 6;
+  const int h = blockIdx.y;
+  const int c = blockIdx.x * 64 + lane;
+  const bf16* wk = a.wk + ((int64_t)h * LHD + dg * 32) * DC + c;
+  float w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = bf16_to_f32(wk[(int64_t)i * DC]);
+  for (int b = 0; b < a.B; ++b) {
+    const u32x4* qv = (const u32x4*)(a.q + ((int64_t)b * a.H + h) * LHD + dg * 32);
+    float acc = 0.0f;
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const u32x4 qq = qv[v4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(bf16_lo(qq[e]), w[v4 * 8 + 2 * e], acc);
+        acc = __builtin_fmaf(bf16_hi(qq[e]), w[v4 * 8 + 2 * e + 1], acc);
+      }
+    }
+    red[dg][lane] = acc;
+    __syncthreads();
+    if (dg == 0) {
+      const float s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+      a.qp[((int64_t)b * a.H + h) * DC + c] = f32_to_bf16(s * a.c2);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- 2. split attention
+template <int DC>
+__device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
+  constexpr int WDC = DC / 4;      // latent channels of one wave
+  constexpr int KS = WDC / 16;     // k-steps of the score MFMA
+  constexpr int DB = WDC / 32;     // 32-channel blocks of U^T
+  constexpr int RCH = DC / 8;      // 16-byte chunks per tile row
+  constexpr int RPI = 64 / RCH;    // tile rows per 1 KB load instruction
+  constexpr int LPW = KT / RPI / 4;  // load instructions per wave per tile
+  static_assert(DC % 128 == 0 && DC <= kMaxDc, "latent width");
+
+  const int split = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int head = hb * HB + l32;
+  const bool hvalid = head < a.H;
+  const int n0 = split * a.kps;
+  const int n1 = min(a.N, n0 + a.kps);
+  const int wd0 = wave * WDC;
+  const bf16* Cb = a.c + (int64_t)b * a.csb;
+  const int64_t csn = a.csn;
+
+  // q' fragments (B operand of S^T = C q'^T): head l32, channels wd0 + 16 ks + 8 hh .. +8
+  bf16x8 qf[KS];
+  {
+    const bf16* qrow = a.qp + ((int64_t)b * a.H + (hvalid ? head : 0)) * DC + wd0 + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = hvalid ? *(const bf16x8*)(qrow + ks * 16) : bf16x8{};
+  }
+
+  // Tile loads: instruction u of wave w fills LDS bytes [1 KB (w LPW + u), +1 KB), i.e.
+  // rows RPI (w LPW + u) .. +RPI-1; lane i writes physical chunk i mod RCH of row
+  // i / RCH, fetching the logical chunk that the swizzle puts there.
+  uint32_t loff[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int row = RPI * (wave * LPW + u) + lane / RCH;
+    const int pc = lane % RCH;
+    const int lc = (pc & ~15) | ((pc & 15) ^ swz(row));
+    loff[u] = (uint32_t)(row * csn * 2 + lc * 16);
+  }
+  auto load_tile = [&](int tile, auto buf) __attribute__((always_inline)) {
+    const int r0 = tile * KT;
+    const int rows = min(KT, a.N - r0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Cb + (int64_t)r0 * csn), (short)0, (int)((int64_t)(rows - 1) * csn * 2 + DC * 2),
+        kBufferDword3);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_void_t*)(cbuf<decltype(buf)::value>() + (wave * LPW + u) * 512), 16, loff[u], 0,
+          0, 0);
+  };
+
+  // score fragment (A operand): row l32, logical chunk wd0/8 + 2 ks + hh
+  auto sread = [&](const bf16* t, int ks) __attribute__((always_inline)) -> bf16x8 {
+    const int lc = wd0 / 8 + 2 * ks + hh;
+    return *(const bf16x8*)(t + l32 * DC + phys_chunk(l32, lc) * 8);
+  };
+  // transposed fragment of U^T = C^T P^T (A operand): lane p of each 16-lane group points
+  // at row 16 kk + 4 hh + p/4 (and that + 8), channels dbase + 4 (p mod 4) .. +3 with
+  // dbase = wd0 + 32 dblk + 16 ((lane / 16) mod 2); the transposing read hands lane p the
+  // channel dbase + p of those four rows: rows 16 kk + 4 hh + {0..3, 8..11} of channel
+  // wd0 + 32 dblk + (lane mod 32), the keys of this lane's P^T registers.
+  const int p16 = lane & 15;
+  auto tread = [&](const bf16* t, int kk, int dblk) __attribute__((always_inline)) -> bf16x8 {
+    const int row = 16 * kk + 4 * hh + (p16 >> 2);
+    const int d0 = wd0 + 32 * dblk + 16 * ((lane >> 4) & 1) + 4 * (p16 & 3);
+    const bf16* lo = t + row * DC + phys_chunk(row, d0 >> 3) * 8 + (d0 & 7);
+    const bf16* hi = t + (row + 8) * DC + phys_chunk(row + 8, d0 >> 3) * 8 + (d0 & 7);
+    const v4i16 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)lo);
+    const v4i16 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)hi);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16 uacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) uacc[i] = f32x16{};
+  float m_run = -INFINITY;  // running max, base-2 units (q' carries scale * log2 e)
+  float l_run = 0.0f;       // this lane half's sum of bf16-rounded weights
+  bf16x2 ones2;
+  ones2[0] = (bf16)1.0f;
+  ones2[1] = (bf16)1.0f;
+
+  const int t_first = n0 / KT;
+  const int t_last = (n1 + KT - 1) / KT;  // exclusive; splits start on tile boundaries
+
+  auto step = [&](int tile, auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    using BP = std::integral_constant<int, P>;
+    using BQ = std::integral_constant<int, 1 - P>;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile in LDS; every wave is done with the other buffers
+    if (tile + 1 < t_last) load_tile(tile + 1, BQ{});
+    const bf16* t = cbuf<P>();
+    // this wave's share of the scores, over its latent channels
+    f32x16 sp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sread(t, ks), qf[ks], sp, 0, 0, 0);
+    f32x4* xs = xbuf<P>();
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v;
+      v[0] = sp[4 * q4]; v[1] = sp[4 * q4 + 1]; v[2] = sp[4 * q4 + 2]; v[3] = sp[4 * q4 + 3];
+      xs[(wave * 4 + q4) * 64 + lane] = v;
+    }
+    __syncthreads();
+    // the whole scores, summed over the four shares in the same order in every wave
+    f32x16 s;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 v = xs[q4 * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const f32x4 x = xs[(w * 4 + q4) * 64 + lane];
+        v[0] += x[0]; v[1] += x[1]; v[2] += x[2]; v[3] += x[3];
+      }
+      s[4 * q4] = v[0]; s[4 * q4 + 1] = v[1]; s[4 * q4 + 2] = v[2]; s[4 * q4 + 3] = v[3];
+    }
+    // rows past the cache end score -inf (zeros were loaded there)
+    if (tile * KT + KT > a.N) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = tile * KT + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= a.N) s[r] = -INFINITY;
+      }
+    }
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = swap_halves_max(mt);
+    const bool grow = mt > m_run + kLazyRescale;
+    if (__any(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - mt) : 1.0f;  // m_run = -inf: 0
+      m_run = grow ? mt : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) uacc[i][r] *= alpha;
+    }
+    // weights, rounded to bf16: the B operand of U^T = C^T P^T for k-steps 0 and 1
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      bf16x2 pp;
+      pp[0] = (bf16)fast_exp2(s[r] - m_run);
+      pp[1] = (bf16)fast_exp2(s[r + 1] - m_run);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run, false);
+      pb[r >> 3][r & 7] = pp[0];
+      pb[r >> 3][(r & 7) + 1] = pp[1];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dblk = 0; dblk < DB; ++dblk)
+        uacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tread(t, kk, dblk), pb[kk], uacc[dblk],
+                                                             0, 0, 0);
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  load_tile(t_first, B0{});
+  int tile = t_first;
+  for (; tile + 1 < t_last; tile += 2) {
+    step(tile, B0{});
+    step(tile + 1, B1{});
+  }
+  if (tile < t_last) step(tile, B0{});
+
+  // ---- partials of this split: (m, l) per head, and this wave's channels of u
+  const float l_tot = swap_halves_sum(l_run);
+  if (!hvalid) return;
+  const int64_t slot = ((int64_t)b * a.H + head) * a.splits + split;
+  if (wave == 0 && hh == 0) {
+    a.ml[2 * slot] = m_run;
+    a.ml[2 * slot + 1] = l_tot;
+  }
+  float* urow = a.u + slot * DC;
+#pragma unroll
+  for (int dblk = 0; dblk < DB; ++dblk)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4 v;
+      v[0] = uacc[dblk][4 * r4]; v[1] = uacc[dblk][4 * r4 + 1];
+      v[2] = uacc[dblk][4 * r4 + 2]; v[3] = uacc[dblk][4 * r4 + 3];
+      *(f32x4*)(urow + wd0 + 32 * dblk + 8 * r4 + 4 * hh) = v;
+    }
+}
+
+// ---------------------------------------------------------------- 3. merge, W_v, gate
+// grid (128 / 32, H); thread t: output channel d0 + t / 8; part p = t mod 8 takes latent
+// channels 64 i + 8 p .. +7 (i = 0 .. DC/64 - 1) of the W_v row and of u.
+template <int DC>
+__global__ __launch_bounds__(NT) void latent_merge_kernel(LatentDecodeArgs a) {
+  constexpr int NI = DC / 64;
+  __shared__ __align__(16) float us[DC];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int d = blockIdx.x * 32 + (tid >> 3);
+  const int p = tid & 7;
+  // this thread's W_v values, kept for every batch row
+  u32x4 wv[NI];
+  {
+    const bf16* wrow = a.wv + ((int64_t)h * LHD + d) * DC + 8 * p;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) wv[i] = *(const u32x4*)(wrow + 64 * i);
+  }
+  constexpr int CPT = DC >= NT ? DC / NT : 1;  // latent channels merged per thread
+  for (int b = 0; b < a.B; ++b) {
+    const int64_t hrow = ((int64_t)b * a.H + h) * a.splits;
+    const float* ml = a.ml + 2 * hrow;
+    float m = -INFINITY;
+    for (int j = 0; j < a.splits; ++j) m = fmaxf(m, ml[2 * j]);
+    float l = 0.0f;
+    float acc[CPT];
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) acc[e] = 0.0f;
+    for (int j = 0; j < a.splits; ++j) {
+      const float mj = ml[2 * j];
+      if (mj == -INFINITY) continue;  // a split with no key (never produced, but exact)
+      const float f = fast_exp2(mj - m);
+      l = __builtin_fmaf(ml[2 * j + 1], f, l);
+      const float* uj = a.u + (hrow + j) * DC;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e)
+        if (tid + NT * e < DC) acc[e] = __builtin_fmaf(uj[tid + NT * e], f, acc[e]);
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e)
+      if (tid + NT * e < DC) us[tid + NT * e] = acc[e] * inv;
+    __syncthreads();
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const f32x4 u0 = *(const f32x4*)(us + 64 * i + 8 * p);
+      const f32x4 u1 = *(const f32x4*)(us + 64 * i + 8 * p + 4);
+      dot = __builtin_fmaf(bf16_lo(wv[i][0]), u0[0], dot);
+      dot = __builtin_fmaf(bf16_hi(wv[i][0]), u0[1], dot);
+      dot = __builtin_fmaf(bf16_lo(wv[i][1]), u0[2], dot);
+      dot = __builtin_fmaf(bf16_hi(wv[i][1]), u0[3], dot);
+      dot = __builtin_fmaf(bf16_lo(wv[i][2]), u1[0], dot);
+      dot = __builtin_fmaf(bf16_hi(wv[i][2]), u1[1], dot);
+      dot = __builtin_fmaf(bf16_lo(wv[i][3]), u1[2], dot);
+      dot = __builtin_fmaf(bf16_hi(wv[i][3]), u1[3], dot);
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    if (p == 0) {
+      const int64_t idx = ((int64_t)b * a.H + h) * LHD + d;
+      float v = dot;
+      if (a.g) v *= sigmoidf_(bf16_to_f32(a.g[idx]));
+      a.o[idx] = f32_to_bf16(v);
+    }
+    __syncthreads();  // us is rewritten for the next batch row
+  }
+}
+
+// Plain kernels around the templated body: the host pass then never instantiates the
+// device-only builtins it uses.
+__global__ __launch_bounds__(NT, 1) void latent_split_kernel_128(LatentDecodeArgs a) {
+  latent_split_body<128>(a);
+}
+__global__ __launch_bounds__(NT, 1) void latent_split_kernel_256(LatentDecodeArgs a) {
+  latent_split_body<256>(a);
+}
+__global__ __launch_bounds__(NT, 1) void latent_split_kernel_512(LatentDecodeArgs a) {
+  latent_split_body<512>(a);
+}
+
+template <int DC>
+hipError_t launch_latent_t(void (*split_kernel)(LatentDecodeArgs), const LatentDecodeArgs& a,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((latent_absorb_kernel<DC>), dim3(DC / 64, a.H), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_kernel, dim3(a.splits, (a.H + HB - 1) / HB, a.B), dim3(NT),
+                     0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((latent_merge_kernel<DC>), dim3(LHD / 32, a.H), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_latent(const LatentDecodeArgs& a, hipStream_t s) {
+  switch (a.DC) {
+    case 128: return launch_latent_t<128>(latent_split_kernel_128, a, s);
+    case 256: return launch_latent_t<256>(latent_split_kernel_256, a, s);
+    case 512: return launch_latent_t<512>(latent_split_kernel_512, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gmla

@@ -58,11 +58,14 @@ int attend_impl(int dtype, int B, int Tq, int Tk, int H, int D, float scale, int
   if (causal != 0 && causal != 1) return GMLA_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O) return GMLA_ERR_INVALID_ARG;
   if (!(scale == scale) || scale <= 0.0f) return GMLA_ERR_INVALID_ARG;
+  if (Tk > kMaxKeys) return GMLA_ERR_UNSUPPORTED;
   PrefillArgs a;
   a.B = B; a.T = Tq; a.Tk = Tk; a.H = H; a.D = D;
   a.scale = scale;
   a.causal = causal;
   a.q = Q; a.k = K; a.v = V; a.g = G; a.o = O;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
   if (q_strides) {
     a.qsb = q_strides[0]; a.qst = q_strides[1]; a.qsh = q_strides[2];
     if (a.qsb < 0 || a.qst < 0 || a.qsh < 0) return GMLA_ERR_INVALID_ARG;
@@ -123,6 +126,64 @@ int gmla_attend_chunk(int dtype, int B, int Tq, int Tk, int H, int D, float scal
                      stream);
 }
 
+int gmla_attend_varlen(int dtype, int B, int H, int D, float scale, int causal, const void* Q,
+                       const int64_t* q_strides, const int* cu_seqlens_q, int max_seqlen_q,
+                       const void* K, const void* V, const int64_t* kv_strides,
+                       const int* cu_seqlens_k, int max_seqlen_k, const void* G, void* O,
+                       void* stream) {
+  if (!valid_dtype(dtype) || B <= 0 || H <= 0 || D <= 0 || max_seqlen_q <= 0 || max_seqlen_k < 0)
+    return GMLA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return GMLA_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !O || !cu_seqlens_q || !cu_seqlens_k) return GMLA_ERR_INVALID_ARG;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4)) return GMLA_ERR_INVALID_ARG;
+  if (!(scale == scale) || scale <= 0.0f) return GMLA_ERR_INVALID_ARG;
+  if (max_seqlen_q > kMaxKeys || max_seqlen_k > kMaxKeys) return GMLA_ERR_UNSUPPORTED;
+  PrefillArgs a;
+  a.B = B; a.T = max_seqlen_q; a.Tk = max_seqlen_k; a.H = H; a.D = D;
+  a.scale = scale;
+  a.causal = causal;
+  a.q = Q; a.k = K; a.v = V; a.g = G; a.o = O;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.qsb = a.sb = 0;  // packed rows: the sequence offsets replace the batch strides
+  if (q_strides) {
+    a.qst = q_strides[0]; a.qsh = q_strides[1];
+    if (a.qst < 0 || a.qsh < 0) return GMLA_ERR_INVALID_ARG;
+  } else {
+    a.qsh = D;
+    a.qst = (int64_t)H * D;
+  }
+  if (kv_strides) {
+    a.st = kv_strides[0]; a.sh = kv_strides[1];
+    if (a.st < 0 || a.sh < 0) return GMLA_ERR_INVALID_ARG;
+  } else {
+    a.sh = D;
+    a.st = (int64_t)H * D;
+  }
+  const size_t es = elem_size(dtype);
+  if (!aligned(Q, es) || !aligned(K, es) || !aligned(V, es) || !aligned(O, es) ||
+      (G && !aligned(G, es)))
+    return GMLA_ERR_INVALID_ARG;
+  if (D != 32 && D != 64 && D != 128) return GMLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == GMLA_BF16 && D == 128) {
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+        (G && !aligned(G, 16)) || a.st % 8 || a.sh % 8 || a.qst % 8 || a.qsh % 8)
+      return GMLA_ERR_INVALID_ARG;
+    if (a.st >= (int64_t)1 << 24) return GMLA_ERR_UNSUPPORTED;
+    if (log_enabled())
+      fprintf(stderr, "gmla: varlen bf16 mfma B=%d max Tq=%d max Tk=%d H=%d causal=%d\n", B,
+              max_seqlen_q, max_seqlen_k, H, causal);
+    e = launch_prefill_bf16_varlen(a, s);
+  } else if (dtype == GMLA_BF16) {
+    e = launch_prefill_simple_bf16(a, s);
+  } else {
+    e = launch_prefill_simple_f32(a, s);
+  }
+  return hip_status(e);
+}
+
 int gmla_decode_num_splits(int B, int H, int N, int D) {
   (void)D;
   if (B <= 0 || H <= 0 || N <= 0) return 1;
@@ -146,15 +207,21 @@ size_t gmla_decode_workspace_bytes(int B, int H, int N, int D, int num_splits) {
   return (size_t)B * H * num_splits * (D + 2) * sizeof(float);
 }
 
-int gmla_attend_decode(int dtype, int B, int H, int N, int D, float scale, const void* Q,
-                       const void* K, const void* V, const int64_t* kv_strides, const void* G,
-                       void* O, void* workspace, size_t workspace_bytes, int num_splits,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the decode entry points: fills `a` (all but the workspace) and
+// the split count.  Returns GMLA_OK or the status the call must return.
+int decode_prepare(int dtype, int B, int H, int N, int D, float scale, const void* Q,
+                   const void* K, const void* V, const int64_t* kv_strides, const void* G,
+                   void* O, int num_splits, DecodeArgs& a) {
   if (!valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 || D <= 0) return GMLA_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O) return GMLA_ERR_INVALID_ARG;
   if (!(scale == scale) || scale <= 0.0f) return GMLA_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > 4096) return GMLA_ERR_INVALID_ARG;
-  DecodeArgs a;
+  // key indices are 32-bit in the kernel: leave room for one step of 1024 rows
+  if (N > kMaxKeys) return GMLA_ERR_UNSUPPORTED;
   a.B = B; a.H = H; a.N = N; a.D = D;
   a.scale = scale;
   a.q = Q; a.k = K; a.v = V; a.g = G; a.o = O;
@@ -176,14 +243,151 @@ int gmla_attend_decode(int dtype, int B, int H, int N, int D, float scale, const
   if (splits > N) splits = N;
   a.splits = splits;
   a.ws = nullptr;
-  if (splits > 1) {
-    const size_t need = gmla_decode_workspace_bytes(B, H, N, D, splits);
+  a.lens = nullptr;
+  return GMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmla_attend_decode(int dtype, int B, int H, int N, int D, float scale, const void* Q,
+                       const void* K, const void* V, const int64_t* kv_strides, const void* G,
+                       void* O, void* workspace, size_t workspace_bytes, int num_splits,
+                       void* stream) {
+  DecodeArgs a;
+  const int st = decode_prepare(dtype, B, H, N, D, scale, Q, K, V, kv_strides, G, O, num_splits, a);
+  if (st != GMLA_OK) return st;
+  if (a.splits > 1) {
+    const size_t need = gmla_decode_workspace_bytes(B, H, N, D, a.splits);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GMLA_ERR_WORKSPACE;
     a.ws = (float*)workspace;
   }
   if (log_enabled())
-    fprintf(stderr, "gmla: decode B=%d H=%d N=%d D=%d splits=%d\n", B, H, N, D, splits);
+    fprintf(stderr, "gmla: decode B=%d H=%d N=%d D=%d splits=%d\n", B, H, N, D, a.splits);
   return hip_status(launch_decode(dtype, a, (hipStream_t)stream));
+}
+
+int gmla_attend_decode_varlen(int dtype, int B, int H, int N, int D, float scale, const void* Q,
+                              const void* K, const void* V, const int64_t* kv_strides,
+                              const int* kv_lens, const void* G, void* O, void* workspace,
+                              size_t workspace_bytes, int num_splits, void* stream) {
+  if (!kv_lens || !aligned(kv_lens, 4)) return GMLA_ERR_INVALID_ARG;
+  DecodeArgs a;
+  const int st = decode_prepare(dtype, B, H, N, D, scale, Q, K, V, kv_strides, G, O, num_splits, a);
+  if (st != GMLA_OK) return st;
+  a.lens = kv_lens;
+  if (a.splits > 1) {
+    const size_t need = gmla_decode_workspace_bytes(B, H, N, D, a.splits);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GMLA_ERR_WORKSPACE;
+    a.ws = (float*)workspace;
+  }
+  if (log_enabled())
+    fprintf(stderr, "gmla: decode varlen B=%d H=%d N<=%d D=%d splits=%d\n", B, H, N, D, a.splits);
+  return hip_status(launch_decode(dtype, a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode over the latent cache
+namespace {
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Key ranges of the latent decode: kps rows each (a multiple of the 32-row tile), and the
+// number of ranges that then covers N with none empty.
+void latent_plan(int B, int H, int N, int num_splits, int* splits, int* kps) {
+  long s = num_splits;
+  if (s <= 0) {
+    // about 512 workgroups of 32 heads, but ranges of at least 128 rows: each range's
+    // partials (d_c + 2 floats per head) cost about what 32 latent rows do
+    const long groups = (long)B * ((H + 31) / 32);
+    s = (512 + groups - 1) / groups;
+    long cap = N / 128;
+    if (cap < 1) cap = 1;
+    if (s > cap) s = cap;
+  }
+  if (s > N) s = N;
+  if (s < 1) s = 1;
+  long k = ((long)N + s - 1) / s;
+  k = (k + 31) / 32 * 32;
+  *kps = (int)k;
+  *splits = (int)(((long)N + k - 1) / k);
+}
+
+size_t latent_ws_bytes(int B, int H, int d_c, int splits) {
+  const size_t heads = (size_t)B * H;
+  return round256(heads * d_c * 2) + round256(heads * splits * 2 * sizeof(float)) +
+         heads * splits * d_c * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmla_decode_latent_num_splits(int B, int H, int N, int d_c) {
+  (void)d_c;
+  if (B <= 0 || H <= 0 || N <= 0) return 1;
+  int splits, kps;
+  latent_plan(B, H, N, 0, &splits, &kps);
+  return splits;
+}
+
+size_t gmla_decode_latent_workspace_bytes(int B, int H, int N, int d_c, int num_splits) {
+  if (B <= 0 || H <= 0 || N <= 0 || d_c <= 0 || num_splits < 0) return 0;
+  int splits, kps;
+  latent_plan(B, H, N, num_splits, &splits, &kps);
+  return latent_ws_bytes(B, H, d_c, splits);
+}
+
+int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, float scale,
+                              const void* Q, const void* C, const int64_t* c_strides,
+                              const void* W_k, const void* W_v, const void* G, void* O,
+                              void* workspace, size_t workspace_bytes, int num_splits,
+                              void* stream) {
+  if (!valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 || D <= 0 || d_c <= 0)
+    return GMLA_ERR_INVALID_ARG;
+  if (!Q || !C || !W_k || !W_v || !O) return GMLA_ERR_INVALID_ARG;
+  if (!(scale == scale) || scale <= 0.0f) return GMLA_ERR_INVALID_ARG;
+  if (num_splits < 0) return GMLA_ERR_INVALID_ARG;
+  LatentDecodeArgs a;
+  if (c_strides) {
+    a.csb = c_strides[0];
+    a.csn = c_strides[1];
+    if (a.csb < 0 || a.csn < 0) return GMLA_ERR_INVALID_ARG;
+  } else {
+    a.csn = d_c;
+    a.csb = (int64_t)N * d_c;
+  }
+  if (!aligned(O, 2) || (G && !aligned(G, 2)) || !aligned(Q, 16) || !aligned(C, 16) ||
+      !aligned(W_k, 16) || !aligned(W_v, 16) || a.csb % 8 || a.csn % 8)
+    return GMLA_ERR_INVALID_ARG;
+  if (dtype != GMLA_BF16 || D != 128 || (d_c != 128 && d_c != 256 && d_c != 512))
+    return GMLA_ERR_UNSUPPORTED;
+  // grid limits (heads and batch rows are grid dimensions), 32-bit row indices, and 32-bit
+  // byte offsets inside one 32-row tile
+  if (N > kMaxKeys || B > 65535 || H > 65535 || a.csn >= ((int64_t)1 << 25))
+    return GMLA_ERR_UNSUPPORTED;
+  latent_plan(B, H, N, num_splits, &a.splits, &a.kps);
+  const size_t heads = (size_t)B * H;
+  const size_t need = latent_ws_bytes(B, H, d_c, a.splits);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return GMLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  a.qp = (bf16*)ws;
+  a.ml = (float*)(ws + round256(heads * d_c * 2));
+  a.u = (float*)(ws + round256(heads * d_c * 2) + round256(heads * a.splits * 2 * sizeof(float)));
+  a.B = B; a.H = H; a.N = N; a.DC = d_c;
+  a.q = (const bf16*)Q;
+  a.c = (const bf16*)C;
+  a.wk = (const bf16*)W_k;
+  a.wv = (const bf16*)W_v;
+  a.g = (const bf16*)G;
+  a.o = (bf16*)O;
+  a.c2 = scale * kLog2e;
+  if (log_enabled())
+    fprintf(stderr, "gmla: decode latent B=%d H=%d N=%d d_c=%d splits=%d (%d rows each)\n", B, H,
+            N, d_c, a.splits, a.kps);
+  return hip_status(launch_decode_latent(a, (hipStream_t)stream));
 }
 
 int gmla_latent_expand(int dtype, int M, int d_c, int d_model, const void* C, const void* W_k,

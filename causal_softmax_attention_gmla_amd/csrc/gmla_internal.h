@@ -18,6 +18,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 constexpr int kWave = 64;
+// Longest key (and query) sequence the kernels take: their row indices are 32-bit, and
+// a workgroup may step up to one tile past the last row, so the host rejects lengths
+// within 16384 of INT32_MAX.
+constexpr int kMaxKeys = 0x7fffffff - (1 << 14);
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies; workgroups are dealt round-robin
 
 // log2(e): softmax is evaluated as 2^(x * scale * log2 e - m), using the hardware 2^x.
@@ -69,8 +73,14 @@ struct PrefillArgs {
   int64_t sb, st, sh;     // element strides of K and V (batch, token, head)
   const void* g;          // nullable gate logits [B, T, H*D]
   void* o;                // [B, T, H*D]
+  // per-sequence lengths (packed rows): sequence b's query rows cu_q[b] .. cu_q[b+1]-1 and
+  // key rows cu_k[b] .. cu_k[b+1]-1 (device arrays); T is then the longest query
+  // sequence and the batch strides are unused.  NULL for equal lengths.
+  const int* cu_q;
+  const int* cu_k;
 };
 hipError_t launch_prefill_bf16_mfma(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16_varlen(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_simple_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_simple_bf16(const PrefillArgs& a, hipStream_t s);
 
@@ -83,8 +93,27 @@ struct DecodeArgs {
   void* o;             // [B, H*D]
   float* ws;           // [B, H, splits, D + 2] partials (m, l, o[D]); NULL when splits == 1
   int splits;
+  const int* lens;     // nullable device [B]: keys held by each row (clamped to [0, N])
 };
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
+
+// Decode over the latent cache (decode_latent.hip).
+struct LatentDecodeArgs {
+  int B, H, N, DC;        // DC: latent width d_c (128, 256 or 512); head width 128
+  int splits, kps;        // key ranges of kps rows (a multiple of 32) each
+  const bf16* q;          // [B, H, 128]
+  const bf16* c;          // latent row (b, n) at b * csb + n * csn, DC contiguous values
+  int64_t csb, csn;
+  const bf16* wk;         // [H * 128, DC]
+  const bf16* wv;         // [H * 128, DC]
+  const bf16* g;          // nullable gate logits [B, H * 128]
+  bf16* o;                // [B, H * 128]
+  float c2;               // scale * log2 e, folded into the absorbed query
+  bf16* qp;               // workspace: absorbed queries [B, H, DC]
+  float* ml;              // workspace: (m, l) per (b, h, split)
+  float* u;               // workspace: [B, H, splits, DC] latent sums
+};
+hipError_t launch_decode_latent(const LatentDecodeArgs& a, hipStream_t s);
 
 struct GemmArgs {
   int M, N, K;

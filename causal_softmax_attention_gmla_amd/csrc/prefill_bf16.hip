@@ -42,6 +42,9 @@
 //  * The queries may be the last T rows of Tk >= T keys (a chunk after a cache):
 //    query i sits at position i + Tk - T and sees the keys up to there ("Kimi K2 -
 //    Construct causal mask": positions continue from the cached length).
+//  * Per-sequence lengths (a packed batch of sequences of different lengths, offsets in
+//    cu_q / cu_k on the device): a second instantiation of the same body reads each
+//    sequence's rows and lengths at entry; its query i sits at position i + Tk_b - Tq_b.
 //  * On a block's last tile a wave skips the 32-key halves that none of its queries may
 //    see (their weights are exactly 0).
 //  * Workgroups are mapped so that all query blocks of one head run on the same XCD
@@ -125,8 +128,8 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, bf16* dst, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, off, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb,
-                                                                   int total, int hgroup) {
+template <bool VARLEN>
+__device__ __forceinline__ void prefill_body(const PrefillArgs& a, int nqb, int total, int hgroup) {
 
   // ---- workgroup -> (head, query block).  Workgroups are dealt to the XCDs round-robin
   // and each XCD takes a contiguous set of heads (their K/V then share that XCD's L2).
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int bid = blockIdx.x;
   const int per_xcd = total / kNumXcd;
   int head_lin, rank;
-  if (bid < per_xcd * kNumXcd && per_xcd % nqb == 0) {
+  if (!VARLEN && bid < per_xcd * kNumXcd && per_xcd % nqb == 0) {
     const int x = bid % kNumXcd, i = bid / kNumXcd;
     const int hx = per_xcd / nqb;  // heads per XCD
     const int G = min(hgroup, hx);
@@ -154,20 +157,42 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int b = head_lin / a.H;
   const int h = head_lin % a.H;
   const int q0 = qb * BM;
-  const int T = a.T;             // query rows
-  const int Tk = a.Tk;           // key rows
-  const int off = a.Tk - a.T;    // position of query 0
+  // Query rows, key rows and the position of query 0.  With per-sequence lengths
+  // (packed rows, offsets in cu_q / cu_k) sequence b owns query rows cu_q[b] ..
+  // cu_q[b+1] - 1 and key rows cu_k[b] .. cu_k[b+1] - 1; its query i sits at position
+  // i + Tk_b - Tq_b.  The launch covers the longest sequence; blocks past a shorter
+  // one's end leave at once.
+  int T, Tk, off;
+  int64_t qrow0;  // row of this sequence's query 0 in Q, G and O (as a token index)
+  const bf16* __restrict__ Qh;
+  const bf16* __restrict__ Kh;
+  const bf16* __restrict__ Vh;
+  if (VARLEN) {
+    const int qlo = a.cu_q[b], klo = a.cu_k[b];
+    T = a.cu_q[b + 1] - qlo;
+    Tk = max(a.cu_k[b + 1] - klo, 0);
+    if (q0 >= T) return;
+    off = Tk - T;
+    qrow0 = qlo;
+    Qh = (const bf16*)a.q + (int64_t)qlo * a.qst + (int64_t)h * a.qsh;
+    Kh = (const bf16*)a.k + (int64_t)klo * a.st + (int64_t)h * a.sh;
+    Vh = (const bf16*)a.v + (int64_t)klo * a.st + (int64_t)h * a.sh;
+  } else {
+    T = a.T;
+    Tk = a.Tk;
+    off = a.Tk - a.T;
+    qrow0 = (int64_t)b * a.T;
+    const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
+    Qh = (const bf16*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
+    Kh = (const bf16*)a.k + head_off;
+    Vh = (const bf16*)a.v + head_off;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-
-  const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const bf16* __restrict__ Qh = (const bf16*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
-  const bf16* __restrict__ Kh = (const bf16*)a.k + head_off;
-  const bf16* __restrict__ Vh = (const bf16*)a.v + head_off;
   const int64_t st = a.st;
 
   // ---- this lane's query row and its Q fragments (B operand of S^T = K Q^T)
@@ -325,6 +350,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) o_acc[i][r] *= alpha;
     }
+    // With per-sequence lengths a query may see no key at all (a sequence with more new
+    // queries than keys): its maximum stays -inf and its weights must come out 0, not
+    // 2^(-inf + inf).
+    const float mneg = (VARLEN && m_run == -INFINITY) ? 0.0f : -m_run;
     if (NEXT != 2) {
       // next tiles in flight straight into LDS: K two tiles ahead (into the buffer K_j
       // used), V one tile ahead; tiles past the end arrive as zeros
@@ -352,8 +381,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     auto eunit = [&](auto U) __attribute__((always_inline)) {
       constexpr int u = decltype(U)::value;
       constexpr int sub = u >> 3, idx = ((u >> 2) & 1) * 8 + (u & 3) * 2;
-      const float p0 = fast_exp2(__builtin_fmaf(s_cur[sub][idx], c2, -m_run));
-      const float p1 = fast_exp2(__builtin_fmaf(s_cur[sub][idx + 1], c2, -m_run));
+      const float p0 = fast_exp2(__builtin_fmaf(s_cur[sub][idx], c2, mneg));
+      const float p1 = fast_exp2(__builtin_fmaf(s_cur[sub][idx + 1], c2, mneg));
       bf16x2 pp;
       pp[0] = (bf16)p0;
       pp[1] = (bf16)p1;
@@ -469,9 +498,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // after the second-to-last tile, and stores whole 256-byte rows from there.  Row r's
   // 16-byte unit u sits at unit u ^ (r mod 16), so neither side meets bank conflicts.
   const float l_tot = swap_halves_sum(l_run);
-  const float inv = 1.0f / l_tot;
+  // (a query with no visible key, possible only with per-sequence lengths, writes zeros)
+  const float inv = VARLEN ? (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) : 1.0f / l_tot;
   const int64_t hd = (int64_t)a.H * HD;
-  const bf16* __restrict__ gate = a.g ? (const bf16*)a.g + ((int64_t)b * T + tq) * hd + (int64_t)h * HD
+  const bf16* __restrict__ gate = a.g ? (const bf16*)a.g + (qrow0 + tq) * hd + (int64_t)h * HD
                                       : nullptr;
   char* const ep = (char*)(wave < 2 ? lds_k0 : lds_k1) + (wave & 1) * 8192;
 #pragma unroll
@@ -495,7 +525,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       w[1] = pack_bf16x2(v2, v3);
       *(u32x2*)(ep + l32 * 256 + (((d >> 3) ^ (l32 & 15)) << 4) + (d & 4) * 2) = w;
     }
-  bf16* __restrict__ out = (bf16*)a.o + ((int64_t)b * T + wq0) * hd + (int64_t)h * HD;
+  bf16* __restrict__ out = (bf16*)a.o + (qrow0 + wq0) * hd + (int64_t)h * HD;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int piece = lane + 64 * k;
@@ -505,7 +535,29 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   }
 }
 
+// Plain kernels around the templated body (the host pass then never instantiates the
+// device-only builtins it uses).
+__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb,
+                                                                   int total, int hgroup) {
+  prefill_body<false>(a, nqb, total, hgroup);
+}
+__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_varlen_kernel(PrefillArgs a, int nqb,
+                                                                          int total, int hgroup) {
+  prefill_body<true>(a, nqb, total, hgroup);
+}
+
 }  // namespace
+
+hipError_t launch_prefill_bf16_varlen(const PrefillArgs& a, hipStream_t s) {
+  // a.T is the longest query sequence: every sequence gets that many query blocks and the
+  // blocks past its own end leave at once; each (sequence, head) stays on one XCD
+  const int nqb = (a.T + BM - 1) / BM;
+  const long total = (long)nqb * a.B * a.H;
+  if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(prefill_bf16_varlen_kernel, dim3((unsigned)total), dim3(NTHREADS), 0, s, a,
+                     nqb, (int)total, 1);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16_mfma(const PrefillArgs& a, hipStream_t s) {
   const int nqb = (a.T + BM - 1) / BM;

@@ -23,7 +23,7 @@ namespace {
 
 constexpr int KT = 64;  // keys per tile
 
-template <typename E, int D, int TPQ>
+template <typename E, int D, int TPQ, bool VARLEN>
 __global__ __launch_bounds__(64) void prefill_simple_kernel(PrefillArgs a) {
   constexpr int DP = D / TPQ;    // channels per lane
   constexpr int QPB = 64 / TPQ;  // queries per workgroup
@@ -39,11 +39,30 @@ __global__ __launch_bounds__(64) void prefill_simple_kernel(PrefillArgs a) {
   const int qi = tid % QPB;   // query slot in the workgroup
   const int part = tid / QPB;  // channel slice
   const int t = qb * QPB + qi;
-  const int T = a.T, Tk = a.Tk, off = a.Tk - a.T;
-  const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
-  const E* Qh = (const E*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
-  const E* Kh = (const E*)a.k + head_off;
-  const E* Vh = (const E*)a.v + head_off;
+  // per-sequence lengths: sequence b owns packed query rows cu_q[b] .. and key rows
+  // cu_k[b] ..; its query i sits at position i + Tk_b - Tq_b
+  int T, Tk;
+  int64_t qrow0;
+  const E *Qh, *Kh, *Vh;
+  if (VARLEN) {
+    const int qlo = a.cu_q[b], klo = a.cu_k[b];
+    T = a.cu_q[b + 1] - qlo;
+    Tk = max(a.cu_k[b + 1] - klo, 0);
+    if (qb * QPB >= T) return;  // the whole workgroup: past this sequence's end
+    qrow0 = qlo;
+    Qh = (const E*)a.q + (int64_t)qlo * a.qst + (int64_t)h * a.qsh;
+    Kh = (const E*)a.k + (int64_t)klo * a.st + (int64_t)h * a.sh;
+    Vh = (const E*)a.v + (int64_t)klo * a.st + (int64_t)h * a.sh;
+  } else {
+    T = a.T;
+    Tk = a.Tk;
+    qrow0 = (int64_t)b * a.T;
+    const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
+    Qh = (const E*)a.q + (int64_t)b * a.qsb + (int64_t)h * a.qsh;
+    Kh = (const E*)a.k + head_off;
+    Vh = (const E*)a.v + head_off;
+  }
+  const int off = Tk - T;
 
   float q[DP], o[DP];
 #pragma unroll
@@ -92,18 +111,19 @@ __global__ __launch_bounds__(64) void prefill_simple_kernel(PrefillArgs a) {
     }
   }
   if (t >= T) return;
-  const int64_t row = ((int64_t)b * T + t) * ((int64_t)a.H * D) + (int64_t)h * D + part * DP;
+  const int64_t row = (qrow0 + t) * ((int64_t)a.H * D) + (int64_t)h * D + part * DP;
   const E* g = a.g ? (const E*)a.g + row : nullptr;
   E* out = (E*)a.o + row;
 #pragma unroll
   for (int i = 0; i < DP; ++i) {
-    float v = o[i] / l;
+    // a query that sees no key (possible only with per-sequence lengths) writes zeros
+    float v = (VARLEN && l == 0.0f) ? 0.0f : o[i] / l;
     if (g) v *= 1.0f / (1.0f + expf(-Elem<E>::load(g + i)));
     Elem<E>::store(out + i, v);
   }
 }
 
-template <typename E>
+template <typename E, bool VARLEN>
 hipError_t launch_simple(const PrefillArgs& a, hipStream_t s) {
   auto go = [&](auto kernel, int qpb) {
     const long nqb = (a.T + qpb - 1) / qpb;
@@ -113,9 +133,9 @@ hipError_t launch_simple(const PrefillArgs& a, hipStream_t s) {
     return hipGetLastError();
   };
   switch (a.D) {
-    case 32: return go(prefill_simple_kernel<E, 32, 1>, 64);
-    case 64: return go(prefill_simple_kernel<E, 64, 1>, 64);
-    case 128: return go(prefill_simple_kernel<E, 128, 2>, 32);
+    case 32: return go(prefill_simple_kernel<E, 32, 1, VARLEN>, 64);
+    case 64: return go(prefill_simple_kernel<E, 64, 1, VARLEN>, 64);
+    case 128: return go(prefill_simple_kernel<E, 128, 2, VARLEN>, 32);
     default: return hipErrorInvalidValue;
   }
 }
@@ -123,10 +143,10 @@ hipError_t launch_simple(const PrefillArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill_simple_f32(const PrefillArgs& a, hipStream_t s) {
-  return launch_simple<float>(a, s);
+  return a.cu_q ? launch_simple<float, true>(a, s) : launch_simple<float, false>(a, s);
 }
 hipError_t launch_prefill_simple_bf16(const PrefillArgs& a, hipStream_t s) {
-  return launch_simple<bf16>(a, s);
+  return a.cu_q ? launch_simple<bf16, true>(a, s) : launch_simple<bf16, false>(a, s);
 }
 
 }  // namespace gmla

@@ -27,6 +27,9 @@
  *     asynchronous and stream-ordered; a launch failure returns GMLA_ERR_HIP.
  *   - The library holds no mutable global state, so calls from several host threads
  *     are safe; calls whose outputs alias their inputs are not supported.
+ *   - Sequence lengths (T, Tq, Tk, N) are at most 2^31 - 16385: the kernels index rows
+ *     with 32-bit integers and may step one tile past the last row; longer sequences
+ *     return GMLA_ERR_UNSUPPORTED.
  *   - Sizes are element counts; strides are element strides.
  */
 #ifndef GMLA_H
@@ -74,8 +77,10 @@ int gmla_version(void);
  *   O       : contiguous [B, T, H*D] output (heads joined back to model width).
  *   scale   : usually 1/sqrt(D) ("Gated MLA", the attention formula).
  * Supported: GMLA_BF16 with D = 128 (MFMA kernel) or D in {32, 64}; GMLA_F32 with
- * D in {32, 64, 128}.  bf16 pointers must be 16-byte aligned, and strides multiples
- * of 8, for D = 128.
+ * D in {32, 64, 128}.  Every pointer must be aligned to its element size.  For bf16
+ * with D = 128: Q, K, V, G and O 16-byte aligned and every stride a multiple of 8
+ * (else GMLA_ERR_INVALID_ARG), and the token stride below 2^24 elements (byte offsets
+ * inside one 64-row key tile are 32-bit; else GMLA_ERR_UNSUPPORTED).
  */
 int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int causal,
                         const void* Q, const void* K, const void* V, const int64_t* strides,
@@ -95,11 +100,38 @@ int gmla_attend_prefill(int dtype, int B, int T, int H, int D, float scale, int 
  *   K,V: element (b, s, h, d) at b*kv_strides[0] + s*kv_strides[1] + h*kv_strides[2] + d
  *       (NULL: contiguous [B, Tk, H, D]), s < Tk: the cache followed by the chunk.
  *   G : nullable, contiguous [B, Tq, H*D];  O : contiguous [B, Tq, H*D].
- * Requires 1 <= Tq <= Tk (else GMLA_ERR_INVALID_ARG).
+ * Requires 1 <= Tq <= Tk (else GMLA_ERR_INVALID_ARG).  Alignment, stride and length
+ * limits as for gmla_attend_prefill (the key token stride is kv_strides[1]).
  */
 int gmla_attend_chunk(int dtype, int B, int Tq, int Tk, int H, int D, float scale, int causal,
                       const void* Q, const int64_t* q_strides, const void* K, const void* V,
                       const int64_t* kv_strides, const void* G, void* O, void* stream);
+
+/*
+ * Attention over a packed batch of sequences of different lengths (ragged prefill or
+ * chunked prefill with a different cached length per sequence).  Sequence b owns the
+ * query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 (Tq_b of them) and the key/value
+ * rows cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1 (Tk_b); its query i sits at position
+ * i + Tk_b - Tq_b, positions continuing from that sequence's cached length ("Kimi K2 -
+ * Construct causal mask"), and with causal = 1 sees its keys s <= i + Tk_b - Tq_b
+ * (bottom-right aligned per sequence); with causal = 0 all Tk_b of them.  Same formula
+ * and gate as gmla_attend_prefill.  A query that sees no key (only possible when
+ * Tq_b > Tk_b) gets an all-zero output row.
+ *
+ *   Q    : row r, head h at r*q_strides[0] + h*q_strides[1] (NULL: contiguous
+ *          [total_q, H, D]);  K, V: likewise with kv_strides ([total_k, H, D]).
+ *   cu_seqlens_q, cu_seqlens_k : DEVICE arrays of B + 1 int32 row offsets,
+ *          non-decreasing; every Tq_b <= max_seqlen_q (rows past it are not computed)
+ *          and every Tk_b <= 2^31 - 16385.  The offsets are read by the kernels only, so
+ *          the caller guarantees they address rows inside Q, K, V, G and O.
+ *   G    : nullable, contiguous [total_q, H*D];  O : contiguous [total_q, H*D].
+ * Supported types, alignment and stride limits as for gmla_attend_prefill.
+ */
+int gmla_attend_varlen(int dtype, int B, int H, int D, float scale, int causal, const void* Q,
+                       const int64_t* q_strides, const int* cu_seqlens_q, int max_seqlen_q,
+                       const void* K, const void* V, const int64_t* kv_strides,
+                       const int* cu_seqlens_k, int max_seqlen_k, const void* G, void* O,
+                       void* stream);
 
 /*
  * Decode: one new query per (b, h) against N cached keys.  The query sits at
@@ -116,8 +148,11 @@ int gmla_attend_chunk(int dtype, int B, int Tq, int Tk, int H, int D, float scal
  *   workspace: device scratch of at least gmla_decode_workspace_bytes(B, H, N, D,
  *        num_splits) bytes (may be NULL when that is 0), owned by the caller, and not
  *        shared with a concurrent call.
- *   num_splits: 0 chooses automatically (gmla_decode_num_splits).
- * Supported: D = 128 (bf16 or f32), or D in {32, 64} (f32 or bf16).
+ *   num_splits: 0 chooses automatically (gmla_decode_num_splits); at most 4096.
+ * Supported: D = 128 (bf16 or f32), or D in {32, 64} (f32 or bf16).  Q, K and V must be
+ * 16-byte aligned and every kv_stride times the element size a multiple of 16 bytes
+ * (rows are read 16 bytes at a time, float32 too); O and G aligned to their element
+ * size.  Else GMLA_ERR_INVALID_ARG.
  */
 int gmla_decode_num_splits(int B, int H, int N, int D);
 size_t gmla_decode_workspace_bytes(int B, int H, int N, int D, int num_splits);
@@ -125,6 +160,56 @@ int gmla_attend_decode(int dtype, int B, int H, int N, int D, float scale, const
                        const void* K, const void* V, const int64_t* kv_strides, const void* G,
                        void* O, void* workspace, size_t workspace_bytes, int num_splits,
                        void* stream);
+
+/*
+ * gmla_attend_decode with a cache length per batch row: row b holds kv_lens[b] keys
+ * (a DEVICE array of B int32; values are clamped to [0, N], N being the cache capacity
+ * that kv_strides describe), and its query sits at position kv_lens[b] - 1, seeing all
+ * of them ("Kimi K2 - Construct causal mask": positions continue from the cached
+ * length).  A row with no key gets an all-zero output.  Workspace, splits (taken over
+ * the capacity N), types and limits as for gmla_attend_decode.
+ */
+int gmla_attend_decode_varlen(int dtype, int B, int H, int N, int D, float scale, const void* Q,
+                              const void* K, const void* V, const int64_t* kv_strides,
+                              const int* kv_lens, const void* G, void* O, void* workspace,
+                              size_t workspace_bytes, int num_splits, void* stream);
+
+/*
+ * Decode over the latent cache: one new query per (b, h) at position N - 1 against N
+ * cached tokens that are stored only as latent rows c_n of width d_c ("Gated MLA",
+ * section "Start from familiar attention": K = C W_k^T, V = C W_v^T; section "Common
+ * mistakes to avoid": the cache is the compact latent tensor C; "Le Transformer et
+ * l'attention", "MLA - compresser en un vecteur latent": 512 values per token).
+ *
+ * Computes, with W_k,h and W_v,h the rows h*D .. h*D + D - 1 of W_k and W_v:
+ *   k_{h,n} = W_k,h c_n,  v_{h,n} = W_v,h c_n,
+ *   O[b, h*D + d] = g * sum_n softmax_n(scale * q_{b,h} . k_{h,n}) v_{h,n}[d],
+ * with the optional gate g = sigmoid(G[b, h*D + d]).  The keys and values are never
+ * formed: the library uses the exact regrouping q'_{b,h} = scale W_k,h^T q_{b,h}
+ * (scores q' . c_n) and o = W_v,h (sum_n p_n c_n), so each step reads the d_c latent
+ * values per token (shared by all heads) and W_k, W_v once.
+ *
+ *   Q   : contiguous [B, H, D].
+ *   C   : latent row (b, n) at b*c_strides[0] + n*c_strides[1], d_c contiguous values
+ *         (NULL strides: contiguous [B, N, d_c]).
+ *   W_k, W_v : contiguous [H*D, d_c] (stored [out, in]).
+ *   G   : nullable, contiguous [B, H*D] gate logits;  O : contiguous [B, H*D].
+ *   workspace: at least gmla_decode_latent_workspace_bytes(B, H, N, d_c, num_splits)
+ *         bytes, 256-byte aligned, owned by the caller, not shared with a concurrent call
+ *         (else GMLA_ERR_WORKSPACE).
+ *   num_splits: key ranges per (b, 32-head block); 0 chooses (the ranges are rounded
+ *         to multiples of 32 rows, so the count used can be smaller than asked).
+ * Supported: GMLA_BF16, D = 128, d_c in {128, 256, 512} (else GMLA_ERR_UNSUPPORTED).
+ * Q, C, W_k, W_v 16-byte aligned, C's strides multiples of 8 (else
+ * GMLA_ERR_INVALID_ARG), c_strides[1] below 2^25, B and H at most 65535.
+ */
+int gmla_decode_latent_num_splits(int B, int H, int N, int d_c);
+size_t gmla_decode_latent_workspace_bytes(int B, int H, int N, int d_c, int num_splits);
+int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, float scale,
+                              const void* Q, const void* C, const int64_t* c_strides,
+                              const void* W_k, const void* W_v, const void* G, void* O,
+                              void* workspace, size_t workspace_bytes, int num_splits,
+                              void* stream);
 
 /*
  * Latent up-projection ("Gated MLA", section "Start from familiar attention":

@@ -53,7 +53,8 @@ def test_status_strings_and_version():
     lib = gm.library()
     assert lib.gmla_version() >= 100
     for code, name in ((0, b"GMLA_OK"), (-1, b"GMLA_ERR_INVALID_ARG"), (-2, b"GMLA_ERR_UNSUPPORTED"),
-                       (-3, b"GMLA_ERR_WORKSPACE"), (-4, b"GMLA_ERR_HIP"), (99, b"GMLA_ERR_UNKNOWN")):
+                       (-3, b"GMLA_ERR_WORKSPACE"), (-4, b"GMLA_ERR_HIP"),
+                       (99, b"GMLA_ERR_UNKNOWN")):
         assert lib.gmla_status_string(code) == name
 
 
@@ -85,6 +86,104 @@ def test_prefill_rejects_misaligned_strides():
     assert _prefill(strides=s) == -1
     neg = (ctypes.c_int64 * 3)(-1, 256, 128)
     assert _prefill(strides=neg) == -1
+
+
+MAX_KEYS = 2 ** 31 - 1 - 2 ** 14  # longest sequence the 32-bit row indices take
+
+
+def test_prefill_rejects_key_stride_past_2_24():
+    """The MFMA kernel's byte offsets inside one 64-row key tile are 32-bit: a token
+    stride of 2^24 elements or more is unsupported (2^24 - 8 is the largest accepted)."""
+    big = (ctypes.c_int64 * 3)(2 ** 30, 2 ** 24, 128)
+    assert _prefill(strides=big) == -2
+    assert _chunk(kv_strides=big) == -2
+
+
+def test_sequence_lengths_past_the_32_bit_row_limit_are_unsupported():
+    assert _prefill(T=MAX_KEYS + 1) == -2
+    assert _chunk(Tq=8, Tk=MAX_KEYS + 1) == -2
+    assert _decode(N=MAX_KEYS + 1) == -2
+    assert _decode(N=2 ** 31 - 1) == -2
+
+
+def _varlen(**kw):
+    a = dict(dtype=1, B=2, H=4, D=128, scale=0.1, causal=1, Q=FAKE, q_strides=None, cu_q=FAKE,
+             max_q=100, K=FAKE, V=FAKE, kv_strides=None, cu_k=FAKE, max_k=300, G=None, O=FAKE,
+             stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_varlen(*a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(B=0), dict(H=0), dict(max_q=0), dict(max_k=-1), dict(causal=3),
+                                 dict(cu_q=None), dict(cu_k=None), dict(cu_q=ctypes.c_void_p((1 << 20) + 2)),
+                                 dict(Q=None), dict(O=None), dict(scale=float("nan")),
+                                 dict(q_strides=(ctypes.c_int64 * 2)(512 + 4, 128)),
+                                 dict(kv_strides=(ctypes.c_int64 * 2)(-512, 128))])
+def test_varlen_rejects_bad_arguments(bad):
+    assert _varlen(**bad) == -1
+
+
+def test_varlen_limits():
+    assert _varlen(D=96) == -2
+    assert _varlen(max_q=MAX_KEYS + 1) == -2
+    assert _varlen(max_k=MAX_KEYS + 1) == -2
+    assert _varlen(kv_strides=(ctypes.c_int64 * 2)(2 ** 24, 128)) == -2
+
+
+def _decode_varlen(**kw):
+    a = dict(dtype=1, B=2, H=4, N=100, D=128, scale=0.1, Q=FAKE, K=FAKE, V=FAKE, kv_strides=None,
+             lens=FAKE, G=None, O=FAKE, ws=None, ws_bytes=0, splits=1, stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_decode_varlen(*a.values())
+
+
+def test_decode_varlen_arguments():
+    assert _decode_varlen(lens=None) == -1
+    assert _decode_varlen(lens=ctypes.c_void_p((1 << 20) + 1)) == -1
+    assert _decode_varlen(N=0) == -1
+    assert _decode_varlen(D=48) == -2
+    assert _decode_varlen(splits=4) == -3
+
+
+def _latent(**kw):
+    a = dict(dtype=1, B=2, H=4, N=100, D=128, d_c=512, scale=0.1, Q=FAKE, C=FAKE, c_strides=None,
+             W_k=FAKE, W_v=FAKE, G=None, O=FAKE, ws=FAKE, ws_bytes=1 << 30, splits=0, stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_decode_latent(*a.values())
+
+
+@pytest.mark.parametrize("bad", [dict(B=0), dict(N=0), dict(H=0), dict(Q=None), dict(C=None),
+                                 dict(W_v=None), dict(O=None), dict(scale=0.0), dict(splits=-1),
+                                 dict(C=ctypes.c_void_p((1 << 20) + 8)),
+                                 dict(c_strides=(ctypes.c_int64 * 2)(100 * 512, 516)),
+                                 dict(c_strides=(ctypes.c_int64 * 2)(-512, 512))])
+def test_decode_latent_rejects_bad_arguments(bad):
+    assert _latent(**bad) == -1
+
+
+def test_decode_latent_limits_and_workspace():
+    lib = gm.library()
+    assert _latent(dtype=0) == -2                    # bf16 only
+    assert _latent(D=64) == -2
+    assert _latent(d_c=64) == -2 and _latent(d_c=384) == -2
+    assert _latent(N=MAX_KEYS + 1) == -2
+    assert _latent(c_strides=(ctypes.c_int64 * 2)(2 ** 40, 2 ** 25)) == -2
+    need = lib.gmla_decode_latent_workspace_bytes(2, 4, 100, 512, 0)
+    assert need > 0
+    assert _latent(ws=None) == -3
+    assert _latent(ws_bytes=need - 1) == -3
+    assert _latent(ws=ctypes.c_void_p((1 << 20) + 16)) == -3  # not 256-byte aligned
+    # ranges are rounded to 32-row tiles: the count used covers N with none empty
+    for B, H, N in ((8, 96, 1001), (4, 96, 131072), (1, 1, 1), (1, 40, 33), (2, 3, 100000)):
+        s = lib.gmla_decode_latent_num_splits(B, H, N, 512)
+        kps = -(-N // s)
+        assert s >= 1 and (s - 1) * (-(-kps // 32) * 32) < N
+    assert lib.gmla_decode_latent_num_splits(8, 96, 1001, 512) == 7
+    # workspace: absorbed queries (bf16), (m, l) and d_c sums per (b, h, range)
+    s = lib.gmla_decode_latent_num_splits(8, 96, 1001, 512)
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert lib.gmla_decode_latent_workspace_bytes(8, 96, 1001, 512, 0) == \
+        r256(768 * 512 * 2) + r256(768 * s * 8) + 768 * s * 512 * 4
 
 
 def _chunk(**kw):
@@ -182,14 +281,51 @@ def test_binding_rejects_cpu_tensors_and_mismatches():
         gm.attend_decode_latent(qd, c, w, w)               # host tensors
 
 
-@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
-def test_valid_call_without_a_device_returns_hip_error():
+NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+try:
+    hip = ctypes.CDLL("libamdhip64.so")
+except OSError:
+    hip = ctypes.CDLL("/opt/rocm/lib/libamdhip64.so")
+n = ctypes.c_int(0)
+if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0:
+    sys.exit(77)  # a device is visible: the fake pointers below must never reach it
+sys.path.insert(0, sys.argv[1])
+import test_boundary as tb
+tb.valid_calls_without_a_device()
+print("no-device calls ok")
+"""
+
+
+def valid_calls_without_a_device():
     """Arguments that pass validation reach the launch; with no HIP device the launch
     fails and the call returns GMLA_ERR_HIP instead of crashing."""
     lib = gm.library()
     assert _prefill() == -4
     assert _chunk() == -4
     assert _decode() == -4
+    assert _latent() == -4
+    assert _varlen() == -4
+    assert _varlen(dtype=0, D=64) == -4
+    assert _decode_varlen() == -4
     assert lib.gmla_linear(1, 64, 64, 64, FAKE, FAKE, FAKE, None) == -4
     assert lib.gmla_latent_expand(1, 64, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -4
     assert lib.gmla_gate_out(1, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -4
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")
+def test_valid_call_without_a_device_returns_hip_error():
+    """Runs the fake-pointer calls in a child process whose environment hides every
+    device, and which exits before them if a device is visible anyway."""
+    import subprocess
+    import sys
+
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", NO_DEVICE_SCRIPT, os.path.join(ROOT, "tests")],
+                       capture_output=True, text=True, env=env, timeout=300,
+                       cwd=ROOT)
+    if r.returncode == 77:
+        pytest.skip("a HIP device is visible")
+    assert r.returncode == 0, r.stdout + r.stderr[-3000:]
+    assert "no-device calls ok" in r.stdout
