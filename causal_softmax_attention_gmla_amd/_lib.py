@@ -16,7 +16,7 @@ GMLA_F32 = 0
 GMLA_BF16 = 1
 
 _STATUS = {0: "GMLA_OK", -1: "GMLA_ERR_INVALID_ARG", -2: "GMLA_ERR_UNSUPPORTED",
-           -3: "GMLA_ERR_WORKSPACE", -4: "GMLA_ERR_HIP"}
+           -3: "GMLA_ERR_WORKSPACE", -4: "GMLA_ERR_HIP", -5: "GMLA_ERR_TOO_LARGE"}
 
 # every symbol gmla.h declares, with its ctypes signature
 _vp = ctypes.c_void_p
@@ -41,6 +41,9 @@ SIGNATURES = {
     "gmla_decode_latent_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "gmla_attend_decode_latent": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i64p, _vp, _vp, _vp,
                                        _vp, _vp, ctypes.c_size_t, _i, _vp]),
+    "gmla_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
+    "gmla_attend_decode_noalloc": (_i, [_i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _i64p, _vp, _vp, _i,
+                                        _vp]),
     "gmla_latent_expand": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gmla_gate_out": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "gmla_linear": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp]),

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "gmla_internal.h"
 
 using namespace gmla;
@@ -38,6 +40,7 @@ const char* gmla_status_string(int status) {
     case GMLA_ERR_UNSUPPORTED: return "GMLA_ERR_UNSUPPORTED";
     case GMLA_ERR_WORKSPACE: return "GMLA_ERR_WORKSPACE";
     case GMLA_ERR_HIP: return "GMLA_ERR_HIP";
+    case GMLA_ERR_TOO_LARGE: return "GMLA_ERR_TOO_LARGE";
     default: return "GMLA_ERR_UNKNOWN";
   }
 }
@@ -284,6 +287,65 @@ int gmla_attend_decode_varlen(int dtype, int B, int H, int N, int D, float scale
   }
   if (log_enabled())
     fprintf(stderr, "gmla: decode varlen B=%d H=%d N<=%d D=%d splits=%d\n", B, H, N, D, a.splits);
+  return hip_status(launch_decode(dtype, a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- decode without allocation
+// For callers that cannot allocate (code under HIP graph capture, tight serving loops):
+// the split partials live in a fixed device array instead of a caller workspace.  Host
+// code never passes the array's name to a kernel (that is a host-side stand-in, not a
+// device address): the device address is looked up once per device, with that device
+// current, and kept.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_lock;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on first use).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GMLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GMLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_lock);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GMLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gmla_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int gmla_attend_decode_noalloc(int dtype, int B, int H, int N, int D, float scale,
+                               const void* Q, const void* K, const void* V,
+                               const int64_t* kv_strides, const void* G, void* O, int num_splits,
+                               void* stream) {
+  DecodeArgs a;
+  const int st = decode_prepare(dtype, B, H, N, D, scale, Q, K, V, kv_strides, G, O, num_splits, a);
+  if (st != GMLA_OK) return st;
+  if (a.splits > 1) {
+    if (gmla_decode_workspace_bytes(B, H, N, D, a.splits) > kScratchBytes) return GMLA_ERR_TOO_LARGE;
+    void* p = nullptr;
+    const int sst = scratch_on_current_device(&p);
+    if (sst != GMLA_OK) return sst;
+    // every (batch, head, split) slot is written before the merge reads it: no clearing
+    a.ws = (float*)p;
+  }
+  if (log_enabled())
+    fprintf(stderr, "gmla: decode (no alloc) B=%d H=%d N=%d D=%d splits=%d\n", B, H, N, D,
+            a.splits);
   return hip_status(launch_decode(dtype, a, (hipStream_t)stream));
 }
 

@@ -25,8 +25,9 @@
  *     returns a negative status and launches nothing.
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls are
  *     asynchronous and stream-ordered; a launch failure returns GMLA_ERR_HIP.
- *   - The library holds no mutable global state, so calls from several host threads
- *     are safe; calls whose outputs alias their inputs are not supported.
+ *   - Apart from the fixed scratch array of gmla_attend_decode_noalloc (see there), the
+ *     library holds no mutable global state, so calls from several host threads are
+ *     safe; calls whose outputs alias their inputs are not supported.
  *   - Sequence lengths (T, Tq, Tk, N) are at most 2^31 - 16385: the kernels index rows
  *     with 32-bit integers and may step one tile past the last row; longer sequences
  *     return GMLA_ERR_UNSUPPORTED.
@@ -49,7 +50,8 @@ typedef enum {
   GMLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad flag, misaligned pointer */
   GMLA_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype the library has no kernel for */
   GMLA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
-  GMLA_ERR_HIP = -4          /* the HIP runtime reported an error (no device, launch failure) */
+  GMLA_ERR_HIP = -4,         /* the HIP runtime reported an error (no device, launch failure) */
+  GMLA_ERR_TOO_LARGE = -5    /* the fixed scratch of a no-allocation call is too small */
 } gmla_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -210,6 +212,26 @@ int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, fl
                               const void* W_k, const void* W_v, const void* G, void* O,
                               void* workspace, size_t workspace_bytes, int num_splits,
                               void* stream);
+
+/*
+ * gmla_attend_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops and harnesses that forbid
+ * allocation).  Same arguments, results and limits as gmla_attend_decode, minus the
+ * workspace: when a head is split, the partials go to a fixed scratch array of
+ * gmla_decode_noalloc_scratch_bytes() bytes (4 MiB) that each GPU holds from its first
+ * such call until the process ends.  A call whose split partials need more
+ * (gmla_decode_workspace_bytes(B, H, N, D, splits) > that size) returns
+ * GMLA_ERR_TOO_LARGE and launches nothing; the automatic split count never needs more
+ * than about 2.2 MB for D = 128.  The call itself allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).  All such calls on one GPU share its array,
+ * which keeps the last call's contents: calls that may overlap in time on one GPU (on
+ * different streams, or from several host threads) race, so serialise them.
+ */
+size_t gmla_decode_noalloc_scratch_bytes(void);
+int gmla_attend_decode_noalloc(int dtype, int B, int H, int N, int D, float scale,
+                               const void* Q, const void* K, const void* V,
+                               const int64_t* kv_strides, const void* G, void* O, int num_splits,
+                               void* stream);
 
 /*
  * Latent up-projection ("Gated MLA", section "Start from familiar attention":

@@ -62,6 +62,12 @@ int main(void) {
   EXPECT(gmla_attend_decode(GMLA_BF16, 2, 4, 100, 128, 0.1f, F, F, F, 0, 0, F, 0, 0, 1, 0), GMLA_ERR_HIP);
   EXPECT(gmla_attend_decode(GMLA_F32, 2, 4, 5000, 128, 0.1f, F, F, F, 0, 0, F, F, 1 << 20, 4, 0), GMLA_ERR_HIP);
   EXPECT(gmla_attend_decode(GMLA_BF16, 2, 4, 0x7fffffff, 128, 0.1f, F, F, F, 0, 0, F, 0, 0, 1, 0), GMLA_ERR_UNSUPPORTED);
+  /* decode without allocation */
+  EXPECT(gmla_attend_decode_noalloc(GMLA_BF16, 8, 96, 4096, 128, 0.1f, F, F, F, 0, 0, F, 4096, 0), GMLA_ERR_TOO_LARGE);
+  EXPECT(gmla_attend_decode_noalloc(GMLA_BF16, 2, 4, 100, 48, 0.1f, F, F, F, 0, 0, F, 1, 0), GMLA_ERR_UNSUPPORTED);
+  EXPECT(gmla_attend_decode_noalloc(GMLA_BF16, 2, 4, 100, 128, 0.1f, F, F, F, 0, 0, F, 1, 0), GMLA_ERR_HIP);
+  EXPECT(gmla_attend_decode_noalloc(GMLA_BF16, 2, 4, 5000, 128, 0.1f, F, F, F, 0, 0, F, 4, 0), GMLA_ERR_HIP);
+  if (gmla_decode_noalloc_scratch_bytes() != ((size_t)4 << 20)) ++failures;
   /* per-sequence lengths */
   EXPECT(gmla_attend_varlen(GMLA_BF16, 2, 4, 128, 0.1f, 1, F, 0, F, 0, F, F, 0, F, 10, 0, F, 0), GMLA_ERR_INVALID_ARG);
   EXPECT(gmla_attend_varlen(GMLA_BF16, 2, 4, 96, 0.1f, 1, F, 0, F, 10, F, F, 0, F, 10, 0, F, 0), GMLA_ERR_UNSUPPORTED);

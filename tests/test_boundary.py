@@ -53,7 +53,7 @@ def test_status_strings_and_version():
     lib = gm.library()
     assert lib.gmla_version() >= 100
     for code, name in ((0, b"GMLA_OK"), (-1, b"GMLA_ERR_INVALID_ARG"), (-2, b"GMLA_ERR_UNSUPPORTED"),
-                       (-3, b"GMLA_ERR_WORKSPACE"), (-4, b"GMLA_ERR_HIP"),
+                       (-3, b"GMLA_ERR_WORKSPACE"), (-4, b"GMLA_ERR_HIP"), (-5, b"GMLA_ERR_TOO_LARGE"),
                        (99, b"GMLA_ERR_UNKNOWN")):
         assert lib.gmla_status_string(code) == name
 
@@ -104,6 +104,25 @@ def test_sequence_lengths_past_the_32_bit_row_limit_are_unsupported():
     assert _chunk(Tq=8, Tk=MAX_KEYS + 1) == -2
     assert _decode(N=MAX_KEYS + 1) == -2
     assert _decode(N=2 ** 31 - 1) == -2
+
+
+def test_decode_noalloc_limits():
+    """The no-allocation decode keeps its split partials in a fixed 4 MiB array: partials
+    beyond it are rejected before any HIP call; validation matches the workspace decode."""
+    lib = gm.library()
+    cap = lib.gmla_decode_noalloc_scratch_bytes()
+    assert cap == 4 << 20
+    B, H, N = 8, 96, 4096
+    assert lib.gmla_decode_workspace_bytes(B, H, N, 128, 4096) > cap
+    assert _noalloc(B=B, H=H, N=N, splits=4096) == -5
+    assert _noalloc(N=0) == -1
+    assert _noalloc(D=48) == -2
+    assert _noalloc(N=MAX_KEYS + 1) == -2
+    assert _noalloc(K=ctypes.c_void_p((1 << 20) + 2)) == -1
+    # every automatic split choice fits: at most (2048 + B*H - 1) slots of D + 2 floats
+    for B, H, N in ((4, 96, 131072), (1, 1, 10 ** 9), (1, 96, 2 ** 30), (2, 1023, 10 ** 8)):
+        s = lib.gmla_decode_num_splits(B, H, N, 128)
+        assert lib.gmla_decode_workspace_bytes(B, H, N, 128, s) <= cap
 
 
 def _varlen(**kw):
@@ -184,6 +203,13 @@ def test_decode_latent_limits_and_workspace():
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert lib.gmla_decode_latent_workspace_bytes(8, 96, 1001, 512, 0) == \
         r256(768 * 512 * 2) + r256(768 * s * 8) + 768 * s * 512 * 4
+
+
+def _noalloc(**kw):
+    a = dict(dtype=1, B=2, H=4, N=100, D=128, scale=0.1, Q=FAKE, K=FAKE, V=FAKE, kv_strides=None,
+             G=None, O=FAKE, splits=1, stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_decode_noalloc(*a.values())
 
 
 def _chunk(**kw):
@@ -304,6 +330,8 @@ def valid_calls_without_a_device():
     assert _prefill() == -4
     assert _chunk() == -4
     assert _decode() == -4
+    assert _noalloc() == -4
+    assert _noalloc(splits=4) == -4  # the scratch lookup fails without a device
     assert _latent() == -4
     assert _varlen() == -4
     assert _varlen(dtype=0, D=64) == -4
