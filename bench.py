@@ -158,6 +158,12 @@ def measure_achievable(torch, dev):
 
     # ~60 ms of warm-up: the clock the matrix cores hold settles only under sustained load
     mavg, _, _ = time_calls(torch, mfma, 20, 60)
+    lib.gmla_probe_mfma_random.argtypes = lib.gmla_probe_mfma.argtypes
+
+    def mfma_random(i):
+        assert lib.gmla_probe_mfma_random(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp) == 0
+
+    ravg_m, _, _ = time_calls(torch, mfma_random, 20, 60)
     nbytes = 2 << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     rblocks = 2048
@@ -170,39 +176,66 @@ def measure_achievable(torch, dev):
     ravg, _, _ = time_calls(torch, read, 10, 10)
     del buf
     return {"mfma_bf16_tflops": round(flops / (mavg * 1e-3) / 1e12, 1),
+            "mfma_bf16_random_tflops": round(flops / (ravg_m * 1e-3) / 1e12, 1),
             "hbm_read_gbps": round(nbytes / (ravg * 1e-3) / 1e9, 1),
             "how": "libgmla_probe.so: register-only v_mfma_f32_32x32x16_bf16 loop (512 x 256 "
-                   "threads, 4 chains per wave); 2 GiB non-temporal 16-byte read stream"}
+                   "threads, 4 chains per wave) on constant operands and on eight rotating sets "
+                   "of random bf16 operands; 2 GiB non-temporal 16-byte read stream"}
+
+
+def host_cpu():
+    """The host's CPU model, its logical CPU count, and the CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
 
 
 def cpu_prefill_baseline(q, k, v, budget_s=12.0):
-    """The oracle on whole heads of the prefill workload until ~budget_s of CPU time."""
+    """The oracle on whole, distinct heads of the prefill workload (a seeded order over all
+    (batch, head) pairs, none repeated) until ~budget_s of CPU time or every head is done."""
     import numpy as np
 
     import oracle
     B, T, H, D = q.shape
     threads = oracle.default_threads()
     oracle.load()
+    order = np.random.default_rng(0).permutation(B * H)
     done_flops, heads, t0 = 0, 0, time.perf_counter()
-    rng = np.random.default_rng(0)
-    while True:
-        b, h = int(rng.integers(B)), int(rng.integers(H))
+    for idx in order:
+        b, h = divmod(int(idx), H)
         qh = q[b, :, h].float().cpu().numpy()
         kh = k[b, :, h].float().cpu().numpy()
         vh = v[b, :, h].float().cpu().numpy()
         oracle.attend_head(qh, kh, vh, 1.0 / math.sqrt(D), True, nthreads=threads)
         done_flops += prefill_flops(1, T, 1, D)
         heads += 1
-        if time.perf_counter() - t0 > budget_s or heads >= B * H:
+        if time.perf_counter() - t0 > budget_s:
             break
     el = time.perf_counter() - t0
     return {"value": round(done_flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{heads} of {B * H} heads (all {T} query rows each) of the prefill workload, "
-                      f"{el:.1f} s including host copies, float64, {threads} threads"}
+            "kind": "oracle", **host_cpu(),
+            "sample": f"{heads} distinct of {B * H} (batch, head) pairs, all {T} query rows each, of "
+                      f"the prefill workload, {el:.1f} s including host copies, float64, "
+                      f"{threads} threads over query rows"}
 
 
 def cpu_decode_baseline(q, k, v, budget_s=6.0):
+    """The oracle on distinct (batch, head) decode rows of the 1001-key workload, the rows
+    spread over a thread pool (the oracle runs one query row per call; its C code releases
+    the interpreter lock), until ~budget_s or every row is done."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
@@ -212,20 +245,24 @@ def cpu_decode_baseline(q, k, v, budget_s=6.0):
     kh_all = k.float().cpu().numpy()
     vh_all = v.float().cpu().numpy()
     qh_all = q.float().cpu().numpy()
-    nbytes, heads, t0 = 0, 0, time.perf_counter()
-    rng = np.random.default_rng(0)
-    while True:
-        b, h = int(rng.integers(B)), int(rng.integers(H))
-        oracle.attend_head(qh_all[b, h][None], kh_all[b, h], vh_all[b, h], 1.0 / math.sqrt(D), True,
-                           nthreads=1)
-        nbytes += decode_bytes(1, 1, N, D)
-        heads += 1
-        if time.perf_counter() - t0 > budget_s or heads >= 4 * B * H:
-            break
+    order = [divmod(int(i), H) for i in np.random.default_rng(0).permutation(B * H)]
+    t0 = time.perf_counter()
+    heads = 0
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        for c0 in range(0, len(order), 4 * threads):
+            chunk = order[c0:c0 + 4 * threads]
+            list(ex.map(lambda bh: oracle.attend_head(qh_all[bh[0], bh[1]][None], kh_all[bh[0], bh[1]],
+                                                      vh_all[bh[0], bh[1]], 1.0 / math.sqrt(D), True,
+                                                      nthreads=1), chunk))
+            heads += len(chunk)
+            if time.perf_counter() - t0 > budget_s:
+                break
     el = time.perf_counter() - t0
-    return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} (batch, head) decode rows of {N} keys, {el:.1f} s, float64, 1 thread "
-                      f"(the oracle runs one query row on one thread)"}
+    nbytes = decode_bytes(1, 1, N, D) * heads
+    return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            **host_cpu(),
+            "sample": f"{heads} distinct of {B * H} (batch, head) decode rows of {N} keys, {el:.1f} s, "
+                      f"float64, {threads} threads (one row per call)"}
 
 
 # ----------------------------------------------------------------------------- profiles
@@ -581,6 +618,9 @@ def main():
             result["roofline"]["achievable"] = ach["mfma_bf16_tflops"]
             result["roofline"]["frac_of_achievable"] = round(
                 result["roofline"]["achieved"] / ach["mfma_bf16_tflops"], 4)
+            result["roofline"]["achievable_random_operands"] = ach["mfma_bf16_random_tflops"]
+            result["roofline"]["frac_of_achievable_random_operands"] = round(
+                result["roofline"]["achieved"] / ach["mfma_bf16_random_tflops"], 4)
         if "decode" in result:
             rl = result["decode"]["roofline"]
             rl["achievable"] = ach["hbm_read_gbps"]

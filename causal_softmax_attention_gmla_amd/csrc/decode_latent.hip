@@ -46,13 +46,30 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
-// One array per buffer, so the compiler can tell a load into one from reads of the other.
+// One array per buffer, so the compiler can tell a load into one from reads of another.
+// Three tile buffers: tile j + 2 is requested while tile j is used.
 __shared__ __align__(16) bf16 lat_c0[KT * kMaxDc];
 __shared__ __align__(16) bf16 lat_c1[KT * kMaxDc];
-__shared__ __align__(16) f32x4 lat_x0[4 * 4 * 64];  // score shares [wave][quad][lane]
-__shared__ __align__(16) f32x4 lat_x1[4 * 4 * 64];
-template <int P> __device__ __forceinline__ bf16* cbuf() { return P ? lat_c1 : lat_c0; }
-template <int P> __device__ __forceinline__ f32x4* xbuf() { return P ? lat_x1 : lat_x0; }
+__shared__ __align__(16) bf16 lat_c2[KT * kMaxDc];
+// score shares [wave][quad][lane]: written after a tile's first barrier and read after its
+// second, so the next tile's first barrier already separates the reads from the rewrite
+__shared__ __align__(16) f32x4 lat_x[4 * 4 * 64];
+template <int P> __device__ __forceinline__ bf16* cbuf() {
+  return P == 0 ? lat_c0 : P == 1 ? lat_c1 : lat_c2;
+}
+
+// s_waitcnt vmcnt(N) (N < 64) leaving the other counters alone.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Workgroup barrier for LDS data: waits for this wave's LDS operations only, so tile loads
+// meant to stay in flight are not waited for (a __syncthreads() would wait for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Swizzle of the 16-byte chunk index inside each group of 16 chunks of a tile row.  The
 // score reads take one chunk of 32 consecutive rows; the transposing reads take four
@@ -79,11 +96,16 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // ---------------------------------------------------------------- 1. absorb W_k into q
-// grid (d_c / 64, H); thread t: latent channel 64 blockIdx.x + t mod 64, head channels
-// [32 (t / 64), 32 (t / 64) + 32).
+// grid (d_c / 64, H); thread t: latent channel c = 64 blockIdx.x + t mod 64 and head
+// channels [32 (t / 64), 32 (t / 64) + 32) of W_k (its 32 values stay in registers).  The
+// queries of head h for up to 32 batch rows at a time are staged in LDS; every thread
+// forms its partial dot products for all of them, and one barrier later the four
+// partials of each (row, c) are summed.  No global load waits inside the row loop.
+constexpr int kAbsorbRows = 32;
 template <int DC>
 __global__ __launch_bounds__(NT) void latent_absorb_kernel(LatentDecodeArgs a) {
-  __shared__ float red[4][64];
+  __shared__ __align__(16) float qs[kAbsorbRows][LHD];
+  __shared__ float red[4][kAbsorbRows][64];
   const int tid = threadIdx.x, lane = tid & 63, dg = tid >> 6;
   const int h = blockIdx.y;
   const int c = blockIdx.x * 64 + lane;
@@ -91,25 +113,38 @@ __global__ __launch_bounds__(NT) void latent_absorb_kernel(LatentDecodeArgs a) {
   float w[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) w[i] = bf16_to_f32(wk[(int64_t)i * DC]);
-  for (int b = 0; b < a.B; ++b) {
-    const u32x4* qv = (const u32x4*)(a.q + ((int64_t)b * a.H + h) * LHD + dg * 32);
-    float acc = 0.0f;
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const u32x4 qq = qv[v4];
+  for (int b0 = 0; b0 < a.B; b0 += kAbsorbRows) {
+    const int nb = min(kAbsorbRows, a.B - b0);
+    __syncthreads();  // qs and red are free again
+    // rows b0 .. b0+nb-1 of q[:, h, :]: 16 pieces of 8 values per row
+    for (int piece = tid; piece < nb * 16; piece += NT) {
+      const int r = piece >> 4, k = piece & 15;
+      const u32x4 v = *(const u32x4*)(a.q + ((int64_t)(b0 + r) * a.H + h) * LHD + 8 * k);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(bf16_lo(qq[e]), w[v4 * 8 + 2 * e], acc);
-        acc = __builtin_fmaf(bf16_hi(qq[e]), w[v4 * 8 + 2 * e + 1], acc);
+        qs[r][8 * k + 2 * e] = bf16_lo(v[e]);
+        qs[r][8 * k + 2 * e + 1] = bf16_hi(v[e]);
       }
     }
-    red[dg][lane] = acc;
     __syncthreads();
-    if (dg == 0) {
-      const float s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-      a.qp[((int64_t)b * a.H + h) * DC + c] = f32_to_bf16(s * a.c2);
+    for (int r = 0; r < nb; ++r) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i4 = 0; i4 < 8; ++i4) {
+        const f32x4 qv = *(const f32x4*)&qs[r][dg * 32 + 4 * i4];
+        acc = __builtin_fmaf(qv[0], w[4 * i4], acc);
+        acc = __builtin_fmaf(qv[1], w[4 * i4 + 1], acc);
+        acc = __builtin_fmaf(qv[2], w[4 * i4 + 2], acc);
+        acc = __builtin_fmaf(qv[3], w[4 * i4 + 3], acc);
+      }
+      red[dg][r][lane] = acc;
     }
     __syncthreads();
+    for (int o = tid; o < nb * 64; o += NT) {
+      const int r = o >> 6, l = o & 63;
+      const float sum = ((red[0][r][l] + red[1][r][l]) + red[2][r][l]) + red[3][r][l];
+      a.qp[((int64_t)(b0 + r) * a.H + h) * DC + blockIdx.x * 64 + l] = f32_to_bf16(sum * a.c2);
+    }
   }
 }
 
@@ -203,25 +238,27 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
 
   auto step = [&](int tile, auto parity) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
-    using BP = std::integral_constant<int, P>;
-    using BQ = std::integral_constant<int, 1 - P>;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // tile in LDS; every wave is done with the other buffers
-    if (tile + 1 < t_last) load_tile(tile + 1, BQ{});
+    // this wave's loads of the tile are done when at most the next tile's are in flight
+    if (tile + 1 < t_last)
+      wait_vmcnt<LPW>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();  // tile in LDS; every wave is done with tile - 1 and the shares
+    if (tile + 2 < t_last) load_tile(tile + 2, std::integral_constant<int, (P + 2) % 3>{});
     const bf16* t = cbuf<P>();
     // this wave's share of the scores, over its latent channels
     f32x16 sp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sread(t, ks), qf[ks], sp, 0, 0, 0);
-    f32x4* xs = xbuf<P>();
+    f32x4* xs = lat_x;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       f32x4 v;
       v[0] = sp[4 * q4]; v[1] = sp[4 * q4 + 1]; v[2] = sp[4 * q4 + 2]; v[3] = sp[4 * q4 + 3];
       xs[(wave * 4 + q4) * 64 + lane] = v;
     }
-    __syncthreads();
+    lds_barrier();
     // the whole scores, summed over the four shares in the same order in every wave
     f32x16 s;
 #pragma unroll
@@ -277,13 +314,17 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
   load_tile(t_first, B0{});
+  if (t_first + 1 < t_last) load_tile(t_first + 1, B1{});
   int tile = t_first;
-  for (; tile + 1 < t_last; tile += 2) {
+  for (; tile + 2 < t_last; tile += 3) {
     step(tile, B0{});
     step(tile + 1, B1{});
+    step(tile + 2, B2{});
   }
   if (tile < t_last) step(tile, B0{});
+  if (tile + 1 < t_last) step(tile + 1, B1{});
 
   // ---- partials of this split: (m, l) per head, and this wave's channels of u
   const float l_tot = swap_halves_sum(l_run);
@@ -306,53 +347,90 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
 }
 
 // ---------------------------------------------------------------- 3. merge, W_v, gate
-// grid (128 / 32, H); thread t: output channel d0 + t / 8; part p = t mod 8 takes latent
-// channels 64 i + 8 p .. +7 (i = 0 .. DC/64 - 1) of the W_v row and of u.
+// grid (128 / 32, H, ceil(B / kMergeRows)); thread t: output channel d = d0 + t / 8; part
+// p = t mod 8 takes latent channels 64 i + 8 p .. +7 (i = 0 .. DC/64 - 1) of the W_v row.
+// For its batch rows the workgroup first turns each row's split maxima into merge weights
+// f_j = 2^(m_j - m) and 1 / l in LDS (one wave per row), then merges u for all its rows
+// with independent loads, and finally multiplies by W_v.
+constexpr int kMergeRows = 2;
+constexpr int kMaxMergeSplits = 1024;
 template <int DC>
 __global__ __launch_bounds__(NT) void latent_merge_kernel(LatentDecodeArgs a) {
   constexpr int NI = DC / 64;
-  __shared__ __align__(16) float us[DC];
-  const int tid = threadIdx.x;
+  __shared__ __align__(16) float us[kMergeRows][DC];
+  __shared__ float fw[kMergeRows][kMaxMergeSplits];
+  __shared__ float inv_l[kMergeRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
+  const int b0 = blockIdx.z * kMergeRows;
+  const int nb = min(kMergeRows, a.B - b0);
+  const int S = a.splits;
+  // this thread's W_v values (issued first: their latency overlaps the merge)
   const int d = blockIdx.x * 32 + (tid >> 3);
   const int p = tid & 7;
-  // this thread's W_v values, kept for every batch row
   u32x4 wv[NI];
   {
     const bf16* wrow = a.wv + ((int64_t)h * LHD + d) * DC + 8 * p;
 #pragma unroll
     for (int i = 0; i < NI; ++i) wv[i] = *(const u32x4*)(wrow + 64 * i);
   }
-  constexpr int CPT = DC >= NT ? DC / NT : 1;  // latent channels merged per thread
-  for (int b = 0; b < a.B; ++b) {
-    const int64_t hrow = ((int64_t)b * a.H + h) * a.splits;
-    const float* ml = a.ml + 2 * hrow;
+  // merge weights: wave r takes batch row b0 + r
+  if (wave < nb) {
+    const float* ml = a.ml + 2 * (((int64_t)(b0 + wave) * a.H + h) * S);
     float m = -INFINITY;
-    for (int j = 0; j < a.splits; ++j) m = fmaxf(m, ml[2 * j]);
-    float l = 0.0f;
-    float acc[CPT];
+    for (int j = lane; j < S; j += 64) m = fmaxf(m, ml[2 * j]);
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) acc[e] = 0.0f;
-    for (int j = 0; j < a.splits; ++j) {
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.0f;
+    for (int j = lane; j < S; j += 64) {
       const float mj = ml[2 * j];
-      if (mj == -INFINITY) continue;  // a split with no key (never produced, but exact)
-      const float f = fast_exp2(mj - m);
+      // a range with no key (never produced) gets weight 0
+      const float f = mj == -INFINITY ? 0.0f : fast_exp2(mj - m);
+      fw[wave][j] = f;
       l = __builtin_fmaf(ml[2 * j + 1], f, l);
-      const float* uj = a.u + (hrow + j) * DC;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (lane == 0) inv_l[wave] = 1.0f / l;
+  }
+  __syncthreads();
+  // merged, normalised u of every row; thread t takes channels t + NT e.  Rows past the
+  // batch end read row 0 with weight 0, so the loads carry no branch and the unrolled
+  // loop keeps all of them in flight.
+  constexpr int CPT = DC >= NT ? DC / NT : 1;
+  const bool cvalid = DC >= NT || tid < DC;
+  const int ct = cvalid ? tid : 0;
+  float acc[kMergeRows][CPT];
+#pragma unroll
+  for (int r = 0; r < kMergeRows; ++r)
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) acc[r][e] = 0.0f;
+  const float* ubase[kMergeRows];
+#pragma unroll
+  for (int r = 0; r < kMergeRows; ++r)
+    ubase[r] = a.u + (((int64_t)(b0 + (r < nb ? r : 0)) * a.H + h) * S) * DC + ct;
+#pragma unroll 4
+  for (int j = 0; j < S; ++j) {
+#pragma unroll
+    for (int r = 0; r < kMergeRows; ++r) {
+      const float f = r < nb ? fw[r][j] : 0.0f;
 #pragma unroll
       for (int e = 0; e < CPT; ++e)
-        if (tid + NT * e < DC) acc[e] = __builtin_fmaf(uj[tid + NT * e], f, acc[e]);
+        acc[r][e] = __builtin_fmaf(ubase[r][(int64_t)j * DC + NT * e], f, acc[r][e]);
     }
-    const float inv = 1.0f / l;
+  }
+#pragma unroll
+  for (int r = 0; r < kMergeRows; ++r)
 #pragma unroll
     for (int e = 0; e < CPT; ++e)
-      if (tid + NT * e < DC) us[tid + NT * e] = acc[e] * inv;
-    __syncthreads();
+      if (r < nb && cvalid) us[r][ct + NT * e] = acc[r][e] * inv_l[r];
+  __syncthreads();
+  for (int r = 0; r < nb; ++r) {
     float dot = 0.0f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const f32x4 u0 = *(const f32x4*)(us + 64 * i + 8 * p);
-      const f32x4 u1 = *(const f32x4*)(us + 64 * i + 8 * p + 4);
+      const f32x4 u0 = *(const f32x4*)(&us[r][64 * i + 8 * p]);
+      const f32x4 u1 = *(const f32x4*)(&us[r][64 * i + 8 * p + 4]);
       dot = __builtin_fmaf(bf16_lo(wv[i][0]), u0[0], dot);
       dot = __builtin_fmaf(bf16_hi(wv[i][0]), u0[1], dot);
       dot = __builtin_fmaf(bf16_lo(wv[i][1]), u0[2], dot);
@@ -366,12 +444,11 @@ __global__ __launch_bounds__(NT) void latent_merge_kernel(LatentDecodeArgs a) {
     dot += __shfl_xor(dot, 2);
     dot += __shfl_xor(dot, 4);
     if (p == 0) {
-      const int64_t idx = ((int64_t)b * a.H + h) * LHD + d;
+      const int64_t idx = ((int64_t)(b0 + r) * a.H + h) * LHD + d;
       float v = dot;
       if (a.g) v *= sigmoidf_(bf16_to_f32(a.g[idx]));
       a.o[idx] = f32_to_bf16(v);
     }
-    __syncthreads();  // us is rewritten for the next batch row
   }
 }
 
@@ -397,7 +474,8 @@ hipError_t launch_latent_t(void (*split_kernel)(LatentDecodeArgs), const LatentD
                      0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((latent_merge_kernel<DC>), dim3(LHD / 32, a.H), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((latent_merge_kernel<DC>),
+                     dim3(LHD / 32, a.H, (a.B + kMergeRows - 1) / kMergeRows), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -370,6 +370,7 @@ void latent_plan(int B, int H, int N, int num_splits, int* splits, int* kps) {
     if (s > cap) s = cap;
   }
   if (s > N) s = N;
+  if (s > 1024) s = 1024;  // the merge keeps one weight per range in LDS
   if (s < 1) s = 1;
   long k = ((long)N + s - 1) / s;
   k = (k + 31) / 32 * 32;

@@ -30,6 +30,52 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* out) 
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The same loop on operands that change from one MFMA to the next: eight register sets
+// of bf16 values spread like N(0, 1) samples (from an integer hash of the lane and set),
+// so the matrix cores see data that toggles like the attention's inputs do.  The chip's
+// power management sets the clock from that switching, so this is the ceiling for
+// random data, where the constant-operand loop above is the ceiling for quiet data.
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// a bf16 pair with random signs and mantissas and exponents between 2^-3 and 2^1
+__device__ __forceinline__ uint32_t rand_bf16x2(uint32_t h) {
+  const uint32_t lo = (h & 0x807fu) | ((124u + ((h >> 8) & 3u)) << 7);
+  const uint32_t hi = ((h >> 16) & 0x807fu) | ((124u + ((h >> 24) & 3u)) << 7);
+  return lo | (hi << 16);
+}
+
+__global__ __launch_bounds__(256) void probe_mfma_random_kernel(int iters, float* out) {
+  bf16x8 a[8], b[8];
+  for (int s = 0; s < 8; ++s) {
+    u32x4 wa, wb;
+    for (int e = 0; e < 4; ++e) {
+      wa[e] = rand_bf16x2(mix32((blockIdx.x * 256 + threadIdx.x) * 64 + s * 8 + e));
+      wb[e] = rand_bf16x2(mix32(0x9e3779b9u ^ ((blockIdx.x * 256 + threadIdx.x) * 64 + s * 8 + e)));
+    }
+    a[s] = __builtin_bit_cast(bf16x8, wa);
+    b[s] = __builtin_bit_cast(bf16x8, wb);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * r], b[2 * r], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * r + 1], b[2 * r], c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * r], b[2 * r + 1], c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * r + 1], b[2 * r + 1], c3, 0, 0, 0);
+    }
+  }
+  float s = 0.0f;
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 constexpr int kReadUnroll = 8;
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ p, size_t n,
@@ -57,6 +103,13 @@ int gmla_probe_mfma(int blocks, int iters, float* out, void* stream) {
   if (blocks <= 0 || iters <= 0 || !out) return -1;
   hipLaunchKernelGGL(probe_mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters,
                      out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int gmla_probe_mfma_random(int blocks, int iters, float* out, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return -1;
+  hipLaunchKernelGGL(probe_mfma_random_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     iters, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

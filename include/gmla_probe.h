@@ -28,6 +28,15 @@ extern "C" {
 int gmla_probe_mfma(int blocks, int iters, float* out, void* stream);
 
 /*
+ * The same loop and work count, but each wave cycles through eight register sets of
+ * random bf16 operands (signs and mantissas from an integer hash, magnitudes 2^-3 to
+ * 2^2), so consecutive MFMAs see changing data as the attention's matrix products do.
+ * The clock the chip holds depends on that switching: this is the matrix-core ceiling
+ * for random data.
+ */
+int gmla_probe_mfma_random(int blocks, int iters, float* out, void* stream);
+
+/*
  * Reads `bytes` (a multiple of 16 * 256 * 8) of device memory at `buf` once with
  * 16-byte non-temporal loads, eight in flight per lane, from `blocks` workgroups of
  * 256 threads; `out` (blocks unsigned ints) is written only where a lane's

@@ -38,7 +38,7 @@ def test_probe_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "gmla_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = set(re.findall(r"\b(gmla_probe_[a-z0-9_]+)\s*\(", text))
-    assert names == {"gmla_probe_mfma", "gmla_probe_read"}
+    assert names == {"gmla_probe_mfma", "gmla_probe_mfma_random", "gmla_probe_read"}
     lib = ctypes.CDLL(os.path.join(ROOT, "causal_softmax_attention_gmla_amd", "libgmla_probe.so"))
     for n in names:
         assert hasattr(lib, n)
@@ -47,6 +47,8 @@ def test_probe_library_exports_its_header():
     lib.gmla_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert lib.gmla_probe_read(FAKE, 1000, 8, FAKE, None) == -1  # not a multiple of the chunk
     assert lib.gmla_probe_mfma(0, 10, FAKE, None) == -1
+    lib.gmla_probe_mfma_random.argtypes = lib.gmla_probe_mfma.argtypes
+    assert lib.gmla_probe_mfma_random(4, 0, FAKE, None) == -1
 
 
 def test_status_strings_and_version():
