@@ -31,7 +31,7 @@ import torch
 from . import _lib
 from ._lib import GMLA_BF16, GMLA_F32, GmlaError, LIB_PATH  # noqa: F401
 
-__all__ = ["attend_prefill", "attend_chunk", "attend_varlen", "attend_decode", "attend_decode_varlen",
+__all__ = ["attend_prefill", "attend_prefill_latent", "prefill_latent_workspace_bytes", "attend_chunk", "attend_varlen", "attend_decode", "attend_decode_varlen",
            "attend_decode_latent", "latent_expand", "gate_out",
            "linear", "gated_mla", "decode_num_splits", "decode_workspace_bytes",
            "decode_latent_num_splits", "decode_latent_workspace_bytes", "library", "GmlaError"]
@@ -117,6 +117,60 @@ def attend_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torc
                                          _ptr(q), _ptr(k), _ptr(v), strides, _ptr(gate), _ptr(out),
                                          _stream(dev, stream))
     _lib.check(st, "gmla_attend_prefill")
+    return out
+
+
+def prefill_latent_workspace_bytes(B: int, T: int, H: int, D: int) -> int:
+    return _lib.load().gmla_prefill_latent_workspace_bytes(B, T, H, D)
+
+
+def attend_prefill_latent(q: torch.Tensor, latent: torch.Tensor, key_up_projection: torch.Tensor,
+                          value_up_projection: torch.Tensor, gate: torch.Tensor | None = None, *,
+                          scale: float | None = None, causal: bool = True,
+                          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """Prefill whose keys and values are rebuilt from the latent rows when attention runs
+    (K = C W_k^T, V = C W_v^T, "Gated MLA", "Start from familiar attention"), in one
+    persistent launch; each head's keys and values are formed once, in the workspace.
+
+    q: [B, T, H, D] with a contiguous last axis; latent: contiguous [B, T, d_c];
+    up-projections contiguous [H*D, d_c]; gate: optional [B, T, H*D].  Returns
+    [B, T, H*D].
+    """
+    if q.dim() != 4 or latent.dim() != 3:
+        raise ValueError("q must be [B, T, H, D] and latent [B, T, d_c]")
+    B, T, H, D = q.shape
+    if latent.shape[:2] != (B, T):
+        raise ValueError("q and latent disagree in batch or sequence length")
+    d_c = latent.shape[2]
+    for w in (key_up_projection, value_up_projection):
+        if w.shape != (H * D, d_c) or not w.is_contiguous():
+            raise ValueError("the up-projections must be contiguous [H*D, d_c]")
+    if q.stride(3) != 1 or not latent.is_contiguous():
+        raise ValueError("q needs a contiguous last axis and latent must be contiguous")
+    if not isinstance(causal, bool):
+        raise TypeError("causal must be a bool")
+    dev = _dev(q, latent, key_up_projection, value_up_projection, gate, out, workspace)
+    _same_dtype(q, latent, key_up_projection, value_up_projection, gate, out)
+    if gate is not None and (gate.shape != (B, T, H * D) or not gate.is_contiguous()):
+        raise ValueError("gate must be a contiguous [B, T, H*D] tensor")
+    if out is None:
+        out = torch.empty((B, T, H * D), dtype=q.dtype, device=dev)
+    elif out.shape != (B, T, H * D) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, T, H*D] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lib = _lib.load()
+    need = lib.gmla_prefill_latent_workspace_bytes(B, T, H, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    strides = (ctypes.c_int64 * 3)(q.stride(0), q.stride(1), q.stride(2))
+    st = lib.gmla_attend_prefill_latent(_dtype(q), B, T, H, D, d_c, float(scale), int(causal),
+                                        _ptr(q), strides, _ptr(latent), _ptr(key_up_projection),
+                                        _ptr(value_up_projection), _ptr(gate), _ptr(out),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(dev, stream))
+    _lib.check(st, "gmla_attend_prefill_latent")
     return out
 
 
@@ -433,14 +487,15 @@ def gated_mla(hidden_states: torch.Tensor, query_projection: torch.Tensor,
               latent_down_projection: torch.Tensor, key_up_projection: torch.Tensor,
               value_up_projection: torch.Tensor, output_gate_projection: torch.Tensor,
               output_projection: torch.Tensor, num_heads: int, causal: bool = True,
-              *, stream=None) -> dict:
+              *, fused_latent: bool = False, stream=None) -> dict:
     """One Gated MLA layer ("Gated MLA", sections "Implementation order" and
     "Requirements"): returns {"output": Y, "latent_cache": C} with Y shaped like the
     hidden states and C [batch, sequence, latent width]; inputs are not modified.
 
     Order: Q = X W_q^T, C = X W_c^T, [K | V] = C [W_k | W_v]^T, G = X W_g^T,
     O~ = sigmoid(G) * attention(Q, K, V) (gate fused in the attention epilogue),
-    Y = O~ W_o^T.
+    Y = O~ W_o^T.  With fused_latent=True the keys and values are rebuilt from C inside
+    the attention launch (attend_prefill_latent) instead of by a separate expansion.
     """
     if not isinstance(causal, bool):
         raise TypeError("causal must be a bool")
@@ -465,9 +520,13 @@ def gated_mla(hidden_states: torch.Tensor, query_projection: torch.Tensor,
     X = X.contiguous()
     Q = linear(X, query_projection, stream=stream)
     C = linear(X, latent_down_projection, stream=stream)
-    K, V = latent_expand(C, key_up_projection, value_up_projection, stream=stream)
     G = linear(X, output_gate_projection, stream=stream)
-    O = attend_prefill(Q.view(B, T, num_heads, D), K.view(B, T, num_heads, D),
-                       V.view(B, T, num_heads, D), G, causal=causal, stream=stream)
+    if fused_latent:
+        O = attend_prefill_latent(Q.view(B, T, num_heads, D), C, key_up_projection,
+                                  value_up_projection, G, causal=causal, stream=stream)
+    else:
+        K, V = latent_expand(C, key_up_projection, value_up_projection, stream=stream)
+        O = attend_prefill(Q.view(B, T, num_heads, D), K.view(B, T, num_heads, D),
+                           V.view(B, T, num_heads, D), G, causal=causal, stream=stream)
     Y = gate_out(O, output_projection, stream=stream)
     return {"output": Y, "latent_cache": C}

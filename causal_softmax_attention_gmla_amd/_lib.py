@@ -29,6 +29,9 @@ SIGNATURES = {
     "gmla_attend_prefill": (_i, [_i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _i64p, _vp, _vp, _vp]),
     "gmla_attend_chunk": (_i, [_i, _i, _i, _i, _i, _i, _f, _i, _vp, _i64p, _vp, _vp, _i64p, _vp,
                                _vp, _vp]),
+    "gmla_prefill_latent_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "gmla_attend_prefill_latent": (_i, [_i, _i, _i, _i, _i, _i, _f, _i, _vp, _i64p, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "gmla_attend_varlen": (_i, [_i, _i, _i, _i, _f, _i, _vp, _i64p, _vp, _i, _vp, _vp, _i64p, _vp,
                                 _i, _vp, _vp, _vp]),
     "gmla_attend_decode_varlen": (_i, [_i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _i64p, _vp, _vp, _vp,

@@ -453,6 +453,99 @@ int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, fl
   return hip_status(launch_decode_latent(a, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- latent-fused prefill
+namespace {
+
+struct LatentPrefillLayout {
+  size_t kv_bytes;  // one of K, V
+  size_t flag_ints;
+  size_t total;
+};
+
+LatentPrefillLayout latent_prefill_layout(int B, int T, int H, int D) {
+  LatentPrefillLayout l;
+  l.kv_bytes = round256((size_t)B * T * H * D * 2);
+  const size_t nE = ((size_t)T + 127) / 128;
+  l.flag_ints = (size_t)B * H * nE + kNumXcd + 1;  // ready flags, per-XCD counters, error word
+  l.total = 2 * l.kv_bytes + l.flag_ints * sizeof(int);
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gmla_prefill_latent_workspace_bytes(int B, int T, int H, int D) {
+  if (B <= 0 || T <= 0 || H <= 0 || D <= 0) return 0;
+  return latent_prefill_layout(B, T, H, D).total;
+}
+
+int gmla_attend_prefill_latent(int dtype, int B, int T, int H, int D, int d_c, float scale,
+                               int causal, const void* Q, const int64_t* q_strides, const void* C,
+                               const void* W_k, const void* W_v, const void* G, void* O,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || B <= 0 || T <= 0 || H <= 0 || D <= 0 || d_c <= 0)
+    return GMLA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return GMLA_ERR_INVALID_ARG;
+  if (!Q || !C || !W_k || !W_v || !O) return GMLA_ERR_INVALID_ARG;
+  if (!(scale == scale) || scale <= 0.0f) return GMLA_ERR_INVALID_ARG;
+  LatentPrefillArgs f;
+  PrefillArgs& a = f.p;
+  if (q_strides) {
+    a.qsb = q_strides[0]; a.qst = q_strides[1]; a.qsh = q_strides[2];
+    if (a.qsb < 0 || a.qst < 0 || a.qsh < 0) return GMLA_ERR_INVALID_ARG;
+  } else {
+    a.qsh = D;
+    a.qst = (int64_t)H * D;
+    a.qsb = (int64_t)T * H * D;
+  }
+  if (!aligned(Q, 16) || !aligned(C, 16) || !aligned(W_k, 16) || !aligned(W_v, 16) ||
+      !aligned(O, 16) || (G && !aligned(G, 16)) || a.qsb % 8 || a.qst % 8 || a.qsh % 8)
+    return GMLA_ERR_INVALID_ARG;
+  if (dtype != GMLA_BF16 || D != 128 || d_c % 32 || d_c > (1 << 20)) return GMLA_ERR_UNSUPPORTED;
+  if (T > kMaxKeys || (int64_t)H * D >= ((int64_t)1 << 24)) return GMLA_ERR_UNSUPPORTED;
+  const LatentPrefillLayout l = latent_prefill_layout(B, T, H, D);
+  const int64_t nE = ((int64_t)T + 127) / 128;
+  if ((int64_t)B * H * nE * 2 > 0x7fffffffLL) return GMLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < l.total || !aligned(workspace, 256)) return GMLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  f.kws = (bf16*)ws;
+  f.vws = (bf16*)(ws + l.kv_bytes);
+  f.flags = (int*)(ws + 2 * l.kv_bytes);
+  f.ntasks_e = (int)(B * H * nE);
+  f.counter = f.flags + f.ntasks_e;
+  f.error = f.flags + f.ntasks_e + kNumXcd;
+  f.nE = (int)nE;
+  f.nqb = (int)nE;  // 128-query blocks, 128-row expansion blocks
+  f.ntasks = f.ntasks_e + B * H * f.nqb;
+  f.c = (const bf16*)C;
+  f.wk = (const bf16*)W_k;
+  f.wv = (const bf16*)W_v;
+  f.DC = d_c;
+  a.B = B; a.T = T; a.Tk = T; a.H = H; a.D = D;
+  a.scale = scale;
+  a.causal = causal;
+  a.q = Q; a.k = f.kws; a.v = f.vws; a.g = G; a.o = O;
+  a.sh = D;
+  a.st = (int64_t)H * D;
+  a.sb = (int64_t)T * H * D;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return GMLA_ERR_HIP;
+  // the task queues are per XCD: the device must expose all eight of them (one partition)
+  if (cus % kNumXcd || cus < 32 * kNumXcd) return GMLA_ERR_UNSUPPORTED;
+  if (log_enabled())
+    fprintf(stderr, "gmla: prefill latent B=%d T=%d H=%d d_c=%d tasks=%d+%d workgroups=%d\n", B, T,
+            H, d_c, f.ntasks_e, f.ntasks - f.ntasks_e, 2 * cus);
+  return hip_status(launch_prefill_latent(f, 2 * cus, (hipStream_t)stream));
+}
+
 int gmla_latent_expand(int dtype, int M, int d_c, int d_model, const void* C, const void* W_k,
                        const void* W_v, void* K, void* V, void* stream) {
   if (!valid_dtype(dtype) || M <= 0 || d_c <= 0 || d_model <= 0) return GMLA_ERR_INVALID_ARG;

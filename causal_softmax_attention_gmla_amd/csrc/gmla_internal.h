@@ -81,6 +81,27 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill_bf16_mfma(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16_varlen(const PrefillArgs& a, hipStream_t s);
+
+// Latent-fused prefill (prefill_bf16.hip): one persistent launch in which expansion tasks
+// write the keys and values of (batch, head, 128 latent rows) into a workspace and
+// attention tasks consume them as soon as their rows are ready.
+struct LatentPrefillArgs {
+  PrefillArgs p;          // attention arguments; p.k and p.v point at the workspace K, V
+  const bf16* c;          // latent [B, T, DC], contiguous
+  const bf16* wk;         // [H * 128, DC]
+  const bf16* wv;         // [H * 128, DC]
+  int DC;                 // latent width (a multiple of 32)
+  bf16* kws;              // workspace keys [B, T, H, 128]
+  bf16* vws;              // workspace values [B, T, H, 128]
+  int* flags;             // [B * H * nE] ready flags, zero at launch
+  int* counter;           // one task counter per XCD (8), zero at launch
+  int* error;             // set nonzero if a wait ran out (never by construction)
+  int nE;                 // 128-row expansion blocks per head: ceil(T / 128)
+  int nqb;                // query blocks per head: ceil(T / 128)
+  int ntasks_e;           // B * H * nE
+  int ntasks;             // ntasks_e + B * H * nqb
+};
+hipError_t launch_prefill_latent(const LatentPrefillArgs& a, int workgroups, hipStream_t s);
 hipError_t launch_prefill_simple_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_simple_bf16(const PrefillArgs& a, hipStream_t s);
 

@@ -129,6 +129,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, bf16* dst, 
 }
 
 template <bool VARLEN>
+__device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b, const int h,
+                                              const int qb);
+
+template <bool VARLEN>
 __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int nqb, int total, int hgroup) {
 
   // ---- workgroup -> (head, query block).  Workgroups are dealt to the XCDs round-robin
@@ -154,8 +158,15 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int nqb, int 
     rank = L % nqb;
   }
   const int qb = a.causal ? nqb - 1 - rank : rank;
-  const int b = head_lin / a.H;
-  const int h = head_lin % a.H;
+  prefill_block<VARLEN>(a, head_lin / a.H, head_lin % a.H, qb);
+}
+
+// One query block: queries qb*BM .. qb*BM + BM - 1 of (batch b, head h), all key tiles it
+// may see.  Leaves LDS in use until it returns (the caller separates two blocks with a
+// barrier).
+template <bool VARLEN>
+__device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b, const int h,
+                                              const int qb) {
   const int q0 = qb * BM;
   // Query rows, key rows and the position of query 0.  With per-sequence lengths
   // (packed rows, offsets in cu_q / cu_k) sequence b owns query rows cu_q[b] ..
@@ -535,6 +546,202 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int nqb, int 
   }
 }
 
+// ---------------------------------------------------------------- latent-fused prefill
+// Keys and values are rebuilt from the latent rows when attention runs ("Gated MLA",
+// section "Start from familiar attention": K = C W_k^T, V = C W_v^T), each 128-row block
+// once per head, inside the same launch as the attention: a persistent grid takes tasks
+// from one counter per XCD, first the expansion tasks (batch, head, block) of that XCD's
+// heads, then their query blocks (heaviest first).  A query block waits for the
+// expansion blocks it reads; a task only waits for tasks taken before it from the same
+// counter, and expansion tasks never wait, so every wait ends.  Expansion results go to
+// a workspace and are read back through the XCD's L2.
+constexpr int EXR = 128;      // latent rows (keys) per expansion task
+constexpr int EXK = 32;       // latent channels per pipeline stage (64-byte LDS rows)
+constexpr int kMaxSpins = 1 << 20;  // about a second: far beyond any expansion task
+
+// Chunk swizzle of a 64-byte LDS row (four 16-byte chunks): rows 4i .. 4i+3 see chunk c at
+// c ^ i mod 4, so 16 consecutive rows reading one chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int ex_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// Keys and values of rows key0 .. key0 + 127 of batch b, head h:
+// out[key][n] = sum_c C[key][c] W[n][c] for n < 128 from W_k,h (keys) and n >= 128 from
+// W_v,h (values), on MFMA (D = W C^T: a lane holds four consecutive n of one key per
+// register quad).  Wave w computes output columns 64 w .. 64 w + 63 for all 128 keys.
+// Stages of 32 latent channels go global -> LDS (LDS-direct loads, two stages deep) in
+// the attention's K buffers (C rows) and V buffers (W rows).
+__device__ __forceinline__ void expand_block(const LatentPrefillArgs& f, int b, int h, int e) {
+  const int T = f.p.T, H = f.p.H, DC = f.DC;
+  const int key0 = e * EXR;
+  const int rows = min(EXR, T - key0);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const bf16* Cb = f.c + ((int64_t)b * T + key0) * DC;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Cb, (short)0, rows * DC * 2, kBufferDword3);
+  // waves 0, 1 load the 128 rows of W_k,h; waves 2, 3 those of W_v,h
+  const bf16* Wb = (wave < 2 ? f.wk : f.wv) + (int64_t)h * HD * DC;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Wb, (short)0, HD * DC * 2, kBufferDword3);
+  // C stage: 128 rows x 64 B = 8 instructions of 16 rows, two per wave; W stage: 256 rows,
+  // four per wave.  Lane i fills row (i / 4) of its 16-row group, physical chunk i mod 4.
+  uint32_t coff[2], woff[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * (2 * wave + u) + (lane >> 2);
+    coff[u] = (uint32_t)(row * DC * 2 + ex_chunk(row, lane & 3) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 16 * (4 * wave + u) + (lane >> 2);  // 0..255 over the four waves
+    woff[u] = (uint32_t)((row & 127) * DC * 2 + ex_chunk(row, lane & 3) * 16);
+  }
+  auto load_stage = [&](int st, auto buf) __attribute__((always_inline)) {
+    constexpr int P = decltype(buf)::value;
+    const int koff = st * EXK * 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rc, (lds_void_t*)(k_buf<P>() + (2 * wave + u) * 512), 16, coff[u], koff, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (lds_void_t*)(v_buf<P>() + (4 * wave + u) * 512), 16, woff[u], koff, 0, 0);
+  };
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // fragment of row r (of a stage's C or W rows), k-step ks: logical chunk 2 ks + hh
+  auto frag = [&](const bf16* base, int r, int ks) __attribute__((always_inline)) -> bf16x8 {
+    return *(const bf16x8*)((const char*)base + r * 64 + ex_chunk(r, 2 * ks + hh) * 16);
+  };
+  auto compute = [&](auto buf) __attribute__((always_inline)) {
+    constexpr int P = decltype(buf)::value;
+    const bf16* cs = k_buf<P>();
+    const bf16* ws = v_buf<P>();
+#pragma unroll
+    for (int ks = 0; ks < EXK / 16; ++ks) {
+      bf16x8 wf[2], cf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wf[i] = frag(ws, 64 * wave + 32 * i + l32, ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cf[j] = frag(cs, 32 * j + l32, ks);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], cf[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  const int ns = DC / EXK;
+  load_stage(0, B0{});
+  for (int st = 0; st < ns; st += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // stage st landed; every wave is done with stage st - 1
+    if (st + 1 < ns) load_stage(st + 1, B1{});
+    compute(B0{});
+    if (st + 1 < ns) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (st + 2 < ns) load_stage(st + 2, B0{});
+      compute(B1{});
+    }
+  }
+  // rows key0 + 32 j + l32; columns n = 64 w + 32 i + 8 (r / 4) + 4 hh + r mod 4
+  bf16* out = (wave < 2 ? f.kws : f.vws) + (int64_t)h * HD;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int key = 32 * j + l32;
+    if (key >= rows) continue;
+    bf16* orow = out + ((int64_t)b * T + key0 + key) * ((int64_t)H * HD);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = (64 * wave + 32 * i + 8 * r4 + 4 * hh) & 127;
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1]);
+        v[1] = pack_bf16x2(acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+        *(u32x2*)(orow + n) = v;
+      }
+  }
+}
+
+// The accelerator die (XCD) this workgroup runs on, from the hardware register XCC_ID.
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kNumXcd - 1);
+}
+
+// Heads are dealt to the XCDs (head_lin mod 8); each XCD takes the tasks of its heads from
+// its own counter: first their expansion blocks, then their query blocks, heaviest first.
+// A head's keys and values are therefore written and read through one die's L2, which is
+// coherent for all of its compute units: the producer only waits for its stores to reach
+// L2 before raising the flag, and the consumer reads the flag around the caches
+// (agent-scope atomics), with no cache writeback or invalidation on either side.
+__global__ __launch_bounds__(NTHREADS, 2) void prefill_latent_kernel(LatentPrefillArgs f) {
+  __shared__ int task_slot;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int heads = f.p.B * f.p.H;
+  const int x = xcd_id();
+  const int nh = (heads - x + kNumXcd - 1) / kNumXcd;  // heads head_lin = x + 8 i
+  const int n_e = nh * f.nE;
+  const int n_all = n_e + nh * f.nqb;
+  int* const counter = f.counter + x;
+  for (;;) {
+    __syncthreads();  // the previous task is done with LDS and task_slot
+    if (tid == 0)
+      task_slot = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = task_slot;
+    if (t >= n_all) break;
+    if (t < n_e) {
+      // expansion task: head-major, so a head's blocks are done together
+      const int head_lin = x + kNumXcd * (t / f.nE), e = t % f.nE;
+      expand_block(f, head_lin / f.p.H, head_lin % f.p.H, e);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are in L2
+      __syncthreads();                // ... and every other wave's
+      if (tid == 0)
+        __hip_atomic_store(f.flags + (int64_t)head_lin * f.nE + e, 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // query block, heaviest first across this XCD's heads
+      const int u = t - n_e;
+      const int rank = u / nh;
+      const int head_lin = x + kNumXcd * (u % nh);
+      const int qb = f.p.causal ? f.nqb - 1 - rank : rank;
+      const int T = f.p.T;
+      const int last = f.p.causal ? min(T - 1, qb * BM + BM - 1) : T - 1;
+      const int need = last / EXR + 1;  // expansion blocks 0 .. need - 1
+      if (tid < 64) {
+        const int* fl = f.flags + (int64_t)head_lin * f.nE;
+        for (int e = lane; e < need; e += 64) {
+          int spins = 0;
+          while (__hip_atomic_load(fl + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > kMaxSpins) {  // cannot happen: the task is older than this one
+              __hip_atomic_store(f.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      prefill_block<false>(f.p, head_lin / f.p.H, head_lin % f.p.H, qb);
+    }
+  }
+}
+
+// Clears the ready flags and the task counter (a kernel, not a memset, so the call stays
+// capturable in a graph).
+__global__ __launch_bounds__(256) void prefill_latent_clear_kernel(int* flags, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) flags[i] = 0;
+}
+
 // Plain kernels around the templated body (the host pass then never instantiates the
 // device-only builtins it uses).
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a, int nqb,
@@ -556,6 +763,17 @@ hipError_t launch_prefill_bf16_varlen(const PrefillArgs& a, hipStream_t s) {
   if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(prefill_bf16_varlen_kernel, dim3((unsigned)total), dim3(NTHREADS), 0, s, a,
                      nqb, (int)total, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_latent(const LatentPrefillArgs& f, int workgroups, hipStream_t s) {
+  // flags, the eight per-XCD counters and the error word are contiguous in the workspace
+  const int n = f.ntasks_e + kNumXcd + 1;
+  hipLaunchKernelGGL(prefill_latent_clear_kernel, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024),
+                     dim3(256), 0, s, f.flags, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_latent_kernel, dim3(workgroups), dim3(NTHREADS), 0, s, f);
   return hipGetLastError();
 }
 

@@ -110,6 +110,33 @@ int gmla_attend_chunk(int dtype, int B, int Tq, int Tk, int H, int D, float scal
                       const int64_t* kv_strides, const void* G, void* O, void* stream);
 
 /*
+ * Causal (or full) prefill whose keys and values are rebuilt from the latent rows when
+ * attention runs ("Gated MLA", section "Start from familiar attention": C is the cached
+ * latent, K = C W_k^T and V = C W_v^T): the same result as gmla_latent_expand followed by
+ * gmla_attend_prefill, in one persistent launch.  Expansion tasks compute the keys and
+ * values of (batch, head, 128 latent rows) once each, into the workspace; attention tasks
+ * (query blocks of 128, heaviest first) start as soon as the rows they read are ready.
+ *
+ *   Q : element (b, t, h, d) at b*q_strides[0] + t*q_strides[1] + h*q_strides[2] + d
+ *       (NULL: contiguous [B, T, H, D]).
+ *   C : contiguous [B, T, d_c] latent rows.  W_k, W_v : contiguous [H*D, d_c].
+ *   G : nullable, contiguous [B, T, H*D] gate logits.  O : contiguous [B, T, H*D].
+ *   workspace: at least gmla_prefill_latent_workspace_bytes(B, T, H, D) bytes, 256-byte
+ *       aligned, owned by the caller (the keys and values, plus ready flags that the
+ *       call clears itself), not shared with a concurrent call (else GMLA_ERR_WORKSPACE).
+ * Supported: GMLA_BF16, D = 128, d_c a multiple of 32 (else GMLA_ERR_UNSUPPORTED); Q, C,
+ * W_k, W_v, G, O 16-byte aligned and Q's strides multiples of 8 (else
+ * GMLA_ERR_INVALID_ARG).  The tasks are queued per accelerator die, so the device must
+ * expose all eight dies of the MI355X (a single partition, 256 compute units; else
+ * GMLA_ERR_UNSUPPORTED).  Launches a small clearing kernel, then the fused kernel.
+ */
+size_t gmla_prefill_latent_workspace_bytes(int B, int T, int H, int D);
+int gmla_attend_prefill_latent(int dtype, int B, int T, int H, int D, int d_c, float scale,
+                               int causal, const void* Q, const int64_t* q_strides, const void* C,
+                               const void* W_k, const void* W_v, const void* G, void* O,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Attention over a packed batch of sequences of different lengths (ragged prefill or
  * chunked prefill with a different cached length per sequence).  Sequence b owns the
  * query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 (Tq_b of them) and the key/value

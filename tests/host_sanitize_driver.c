@@ -68,6 +68,13 @@ int main(void) {
   EXPECT(gmla_attend_decode_noalloc(GMLA_BF16, 2, 4, 100, 128, 0.1f, F, F, F, 0, 0, F, 1, 0), GMLA_ERR_HIP);
   EXPECT(gmla_attend_decode_noalloc(GMLA_BF16, 2, 4, 5000, 128, 0.1f, F, F, F, 0, 0, F, 4, 0), GMLA_ERR_HIP);
   if (gmla_decode_noalloc_scratch_bytes() != ((size_t)4 << 20)) ++failures;
+  /* latent-fused prefill */
+  {
+    const size_t need = gmla_prefill_latent_workspace_bytes(1, 300, 2, 128);
+    EXPECT(gmla_attend_prefill_latent(GMLA_BF16, 1, 300, 2, 128, 100, 0.1f, 1, F, 0, F, F, F, 0, F, F, need, 0), GMLA_ERR_UNSUPPORTED);
+    EXPECT(gmla_attend_prefill_latent(GMLA_BF16, 1, 300, 2, 128, 512, 0.1f, 1, F, 0, F, F, F, 0, F, F, need - 1, 0), GMLA_ERR_WORKSPACE);
+    EXPECT(gmla_attend_prefill_latent(GMLA_BF16, 1, 300, 2, 128, 512, 0.1f, 1, F, 0, F, F, F, F, F, F, need, 0), GMLA_ERR_HIP);
+  }
   /* per-sequence lengths */
   EXPECT(gmla_attend_varlen(GMLA_BF16, 2, 4, 128, 0.1f, 1, F, 0, F, 0, F, F, 0, F, 10, 0, F, 0), GMLA_ERR_INVALID_ARG);
   EXPECT(gmla_attend_varlen(GMLA_BF16, 2, 4, 96, 0.1f, 1, F, 0, F, 10, F, F, 0, F, 10, 0, F, 0), GMLA_ERR_UNSUPPORTED);

@@ -166,6 +166,31 @@ def test_decode_varlen_arguments():
     assert _decode_varlen(splits=4) == -3
 
 
+def _platent(**kw):
+    a = dict(dtype=1, B=1, T=300, H=2, D=128, d_c=512, scale=0.1, causal=1, Q=FAKE, q_strides=None,
+             C=FAKE, W_k=FAKE, W_v=FAKE, G=None, O=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_prefill_latent(*a.values())
+
+
+def test_prefill_latent_arguments():
+    lib = gm.library()
+    need = lib.gmla_prefill_latent_workspace_bytes(1, 300, 2, 128)
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert need == 2 * r256(300 * 2 * 128 * 2) + 4 * (2 * 3 + 8 + 1)
+    for bad in (dict(B=0), dict(T=0), dict(causal=2), dict(Q=None), dict(C=None), dict(O=None),
+                dict(scale=0.0), dict(C=ctypes.c_void_p((1 << 20) + 8)),
+                dict(q_strides=(ctypes.c_int64 * 3)(300 * 256, 256 + 4, 128))):
+        assert _platent(**bad) == -1, bad
+    assert _platent(dtype=0) == -2
+    assert _platent(d_c=100) == -2
+    assert _platent(D=64) == -2
+    assert _platent(T=MAX_KEYS + 1) == -2
+    assert _platent(ws=None) == -3
+    assert _platent(ws_bytes=need - 1) == -3
+    assert _platent(ws=ctypes.c_void_p((1 << 20) + 16)) == -3
+
+
 def _latent(**kw):
     a = dict(dtype=1, B=2, H=4, N=100, D=128, d_c=512, scale=0.1, Q=FAKE, C=FAKE, c_strides=None,
              W_k=FAKE, W_v=FAKE, G=None, O=FAKE, ws=FAKE, ws_bytes=1 << 30, splits=0, stream=None)
@@ -335,6 +360,7 @@ def valid_calls_without_a_device():
     assert _noalloc() == -4
     assert _noalloc(splits=4) == -4  # the scratch lookup fails without a device
     assert _latent() == -4
+    assert _platent() == -4
     assert _varlen() == -4
     assert _varlen(dtype=0, D=64) == -4
     assert _decode_varlen() == -4

@@ -225,6 +225,25 @@ def test_layer_t2048_tokens():
     check_rows_rel(host(res["output"][:, rows]), ref["output"], 12288)
 
 
+def test_layer_t2048_fused_latent_tokens():
+    """The full layer (B=1, T=2048, d_model=12288, d_c=512) with the keys and values
+    rebuilt from the latent inside the attention launch: 64 tokens over every GEMM tile
+    against the oracle layer, and the whole output equal to the two-launch layer's."""
+    dev = need_gpu()
+    announce("layer_t2048 fused latent, 64 tokens")
+    x, ws = I.workload_inputs("layer_t2048", dev)
+    H = I.WORKLOADS["layer_t2048"].dims["H"]
+    args = (x, ws["Wq"], ws["Wc"], ws["Wk"], ws["Wv"], ws["Wg"], ws["Wo"], H, True)
+    res = gm.gated_mla(*args, fused_latent=True)
+    two = gm.gated_mla(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(res["output"], two["output"])
+    rows = layer_rows()
+    ref = oracle.gated_mla_layer(host(x), *(host(ws[n]) for n in ("Wq", "Wc", "Wk", "Wv", "Wg", "Wo")),
+                                 H, True, rows=rows)
+    check_rows_rel(host(res["output"][:, rows]), ref["output"], 12288)
+
+
 @pytest.mark.parametrize("B,T,H", [(1, 5120, 40), (1, 3584, 56)])
 def test_prefill_partial_last_head_group(B, T, H):
     """More than three query blocks per workgroup slot on each XCD (200 and 196 blocks per

@@ -660,3 +660,92 @@ def test_decode_varlen(splits, dtype):
                 check_f32_abs(got[b, h][None], ref)
             else:
                 check_rows_rel(got[b, h][None], ref, D)
+
+
+# ---------------------------------------------------------------- latent-fused prefill
+
+
+def latent_prefill_inputs(B, T, H, dc, dev, seed, gate):
+    D = 128
+    q = I.normal((B, T, H, D), torch.bfloat16, dev, seed=seed)
+    c = I.normal((B, T, dc), torch.bfloat16, dev, seed=seed + 1)
+    wk = I.normal((H * D, dc), torch.bfloat16, dev, seed=seed + 2, std=dc ** -0.5)
+    wv = I.normal((H * D, dc), torch.bfloat16, dev, seed=seed + 3, std=dc ** -0.5)
+    g = I.normal((B, T, H * D), torch.bfloat16, dev, seed=seed + 4) if gate else None
+    return q, c, wk, wv, g
+
+
+def oracle_latent_prefill(q, c, wk, wv, g, causal):
+    """The oracle's composition: K = C W_k^T and V = C W_v^T in double for every head,
+    then each head's attention, the heads joined, then the gate."""
+    B, T, H, D = q.shape
+    hq, hc, hwk, hwv = host(q), host(c), host(wk), host(wv)
+    out = np.empty((B, T, H * D))
+    for b in range(B):
+        K = oracle.linear(hc[b], hwk)
+        V = oracle.linear(hc[b], hwv)
+        for h in range(H):
+            sl = slice(h * D, (h + 1) * D)
+            out[b, :, sl] = oracle.attend_head(hq[b, :, h], K[:, sl], V[:, sl], 1 / np.sqrt(D), causal)
+    if g is not None:
+        out = oracle.gate(host(g), out)
+    return out
+
+
+@pytest.mark.parametrize("B,T,H,dc,causal,gate", [
+    (2, 300, 3, 64, True, True), (1, 129, 2, 512, True, False), (2, 1, 4, 128, True, True),
+    (1, 64, 2, 32, False, False), (1, 517, 5, 512, True, True), (3, 256, 2, 96, False, True)])
+def test_prefill_latent(B, T, H, dc, causal, gate):
+    """Keys and values rebuilt from the latent inside the attention launch, every element
+    against the oracle's composition: ragged lengths (1, 129, 300, 517 against 128-row
+    blocks), latent widths 32 to 512, causal and not, gated and not.  The launch's error
+    word (set only if a wait for an expansion ran out) stays 0."""
+    dev = need_gpu()
+    announce(f"prefill latent B={B} T={T} H={H} d_c={dc} causal={causal} gate={gate}")
+    q, c, wk, wv, g = latent_prefill_inputs(B, T, H, dc, dev, 9100 + T + dc, gate)
+    need = gm.prefill_latent_workspace_bytes(B, T, H, 128)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=dev)
+    out = torch.full((B, T, H * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.attend_prefill_latent(q, c, wk, wv, g, causal=causal, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    assert int(ws[-4:].view(torch.int32).item()) == 0  # error word (the workspace's last int)
+    check_rows_rel(host(out), oracle_latent_prefill(q, c, wk, wv, g, causal), 128)
+
+
+@pytest.mark.parametrize("dc", [64, 512])
+def test_prefill_latent_matches_expand_then_prefill_bitwise(dc):
+    """The fused launch forms each key and value with the same products in the same order
+    as the latent expansion, and attends with the same kernel code: bitwise equal to
+    latent_expand followed by attend_prefill, on two calls in a row (the workspace's
+    flags are cleared by each call)."""
+    dev = need_gpu()
+    announce(f"prefill latent vs expand + prefill d_c={dc}")
+    B, T, H = 2, 700, 3
+    q, c, wk, wv, g = latent_prefill_inputs(B, T, H, dc, dev, 9200 + dc, True)
+    K, V = gm.latent_expand(c, wk, wv)
+    ref = gm.attend_prefill(q, K.view(B, T, H, 128), V.view(B, T, H, 128), g)
+    ws = torch.empty(gm.prefill_latent_workspace_bytes(B, T, H, 128), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        got = gm.attend_prefill_latent(q, c, wk, wv, g, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gated_mla_layer_fused_latent(causal):
+    """The layer with the keys and values rebuilt inside the attention launch, against
+    the oracle layer, and equal to the two-launch layer."""
+    dev = need_gpu()
+    announce(f"gated_mla fused latent causal={causal}")
+    B, T, dm, H, dc = 2, 200, 384, 3, 128
+    x, ws = I.layer_inputs(B, T, dm, dc, torch.bfloat16, dev, seed=9300)
+    res = gm.gated_mla(x, ws["Wq"], ws["Wc"], ws["Wk"], ws["Wv"], ws["Wg"], ws["Wo"], H, causal,
+                       fused_latent=True)
+    two = gm.gated_mla(x, ws["Wq"], ws["Wc"], ws["Wk"], ws["Wv"], ws["Wg"], ws["Wo"], H, causal)
+    torch.cuda.synchronize()
+    ref = oracle.gated_mla_layer(host(x), *(host(ws[n]) for n in ("Wq", "Wc", "Wk", "Wv", "Wg", "Wo")),
+                                 H, causal)
+    check_rows_rel(host(res["output"]), ref["output"], dm)
+    assert torch.equal(res["latent_cache"], two["latent_cache"])
+    assert torch.equal(res["output"], two["output"])
