@@ -462,8 +462,10 @@ def gate_out(o_tilde: torch.Tensor, w_o: torch.Tensor | None = None, gate: torch
 
 
 def linear(x: torch.Tensor, w: torch.Tensor, *, out: torch.Tensor | None = None,
-           stream=None) -> torch.Tensor:
-    """x [..., K] times w [N, K] transposed -> [..., N]."""
+           split_k: bool = True, stream=None) -> torch.Tensor:
+    """x [..., K] times w [N, K] transposed -> [..., N].  With split_k (the default), a
+    bf16 product with few output tiles and a deep K (the latent down-projection) splits
+    its reduction over a workspace allocated here (gmla_linear_ws)."""
     K = x.shape[-1]
     N = w.shape[0]
     if w.dim() != 2 or w.shape[1] != K:
@@ -477,8 +479,15 @@ def linear(x: torch.Tensor, w: torch.Tensor, *, out: torch.Tensor | None = None,
         out = torch.empty((*x.shape[:-1], N), dtype=x.dtype, device=dev)
     elif out.shape != (*x.shape[:-1], N) or not out.is_contiguous():
         raise ValueError("out has the wrong shape")
-    st = _lib.load().gmla_linear(_dtype(x), M, N, K, _ptr(x), _ptr(w), _ptr(out),
-                                 _stream(dev, stream))
+    lib = _lib.load()
+    need = lib.gmla_linear_workspace_bytes(M, N, K) if split_k and x.dtype == torch.bfloat16 else 0
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        st = lib.gmla_linear_ws(_dtype(x), M, N, K, _ptr(x), _ptr(w), _ptr(out), _ptr(ws), need,
+                                _stream(dev, stream))
+        _lib.check(st, "gmla_linear_ws")
+        return out
+    st = lib.gmla_linear(_dtype(x), M, N, K, _ptr(x), _ptr(w), _ptr(out), _stream(dev, stream))
     _lib.check(st, "gmla_linear")
     return out
 

@@ -79,6 +79,10 @@ __shared__ __align__(16) bf16 deep_x0[256 * BK];
 __shared__ __align__(16) bf16 deep_x1[256 * BK];
 __shared__ __align__(16) bf16 deep_w0[384 * BK];
 __shared__ __align__(16) bf16 deep_w1[384 * BK];
+__shared__ __align__(16) bf16 split_x0[128 * BK];
+__shared__ __align__(16) bf16 split_x1[128 * BK];
+__shared__ __align__(16) bf16 split_w0[128 * BK];
+__shared__ __align__(16) bf16 split_w1[128 * BK];
 __shared__ __align__(16) bf16 narrow_x0[64 * BK];
 __shared__ __align__(16) bf16 narrow_x1[64 * BK];
 __shared__ __align__(16) bf16 narrow_x2[64 * BK];
@@ -97,6 +101,10 @@ template <> struct StageSet<256, 384, 2> {
   template <int B> static __device__ __forceinline__ bf16* x() { return B == 0 ? deep_x0 : deep_x1; }
   template <int B> static __device__ __forceinline__ bf16* w() { return B == 0 ? deep_w0 : deep_w1; }
 };
+template <> struct StageSet<128, 128, 2> {
+  template <int B> static __device__ __forceinline__ bf16* x() { return B == 0 ? split_x0 : split_x1; }
+  template <int B> static __device__ __forceinline__ bf16* w() { return B == 0 ? split_w0 : split_w1; }
+};
 template <> struct StageSet<64, 64, 4> {
   template <int B> static __device__ __forceinline__ bf16* x() {
     return B == 0 ? narrow_x0 : B == 1 ? narrow_x1 : B == 2 ? narrow_x2 : narrow_x3;
@@ -106,7 +114,7 @@ template <> struct StageSet<64, 64, 4> {
   }
 };
 
-template <int BM, int BN, int S, int WGM, int WGN>
+template <int BM, int BN, int S, int WGM, int WGN, bool SPLIT = false>
 __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nmb, int total) {
   using C = Cfg<BM, BN, S, WGM, WGN>;
   auto xbuf = [&](auto b) __attribute__((always_inline)) -> bf16* {
@@ -122,8 +130,11 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
   const int bid = blockIdx.x;
   const int per_xcd = total / kNumXcd;
   const int L = bid < per_xcd * kNumXcd ? (bid % kNumXcd) * per_xcd + bid / kNumXcd : bid;
-  const int mb = L % nmb;
-  int nblk = L / nmb;
+  // split-K: the ranges of one tile are neighbours in L (the same XCD)
+  const int split = SPLIT ? L % p.splits : 0;
+  const int tile = SPLIT ? L / p.splits : L;
+  const int mb = tile % nmb;
+  int nblk = tile / nmb;
   const bf16* W = (const bf16*)p.w;
   bf16* Y = (bf16*)p.y;
   int N = p.N;
@@ -165,8 +176,9 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
 #pragma unroll
     for (int u = 0; u < C::WL; ++u) wo[u] = offset(8 * (wave * C::WL + u) + (lane >> 3), lane);
   }
+  const int kst0 = SPLIT ? split * p.kps : 0;  // first k stage of this range
   auto load_stage = [&](int kt, auto b) __attribute__((always_inline)) {
-    const int koff = kt * BK * 2;
+    const int koff = (kst0 + kt) * BK * 2;
     const int ln = kKeepOffsets ? lane : opaque(lane);
 #pragma unroll
     for (int u = 0; u < C::XL; ++u)
@@ -218,7 +230,7 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
   };
 
   // ---- pipeline: stage kt is requested at iteration kt - (S - 1)
-  const int nk = K / BK;
+  const int nk = SPLIT ? min(p.kps, K / BK - kst0) : K / BK;
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
@@ -274,6 +286,25 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
   // LDS in chunks of 64 columns: every wave writes its part of the chunk into the first
   // X stage buffer (now idle; rows of 128 bytes, 16-byte unit q of row r at
   // q ^ ((r >> 1) & 7)), then the workgroup stores whole 128-byte row segments.
+  if constexpr (SPLIT) {
+    // float partials of this range: row m holds four consecutive columns per quad
+    float* part = p.part + (int64_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) {
+        const int m = m0 + wm * C::TM + j * 32 + l32;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int n = n0 + wn * C::TN + i * 32 + 8 * r4 + 4 * hh;
+          f32x4 v;
+          v[0] = acc[i][j][4 * r4]; v[1] = acc[i][j][4 * r4 + 1];
+          v[2] = acc[i][j][4 * r4 + 2]; v[3] = acc[i][j][4 * r4 + 3];
+          if (m < M && n < N) *(f32x4*)(part + (int64_t)m * N + n) = v;
+        }
+      }
+    return;
+  }
   static_assert(BN % 64 == 0, "64-column chunks");
   char* const stage = (char*)xbuf(B0{});  // BM rows x 64 bf16
 #pragma unroll
@@ -323,6 +354,30 @@ __global__ __launch_bounds__(256, 2) void gemm_lds_narrow_kernel(GemmArgs p, int
   gemm_lds_body<64, 64, 4, 2, 2>(p, nb1, nmb, total);
 }
 
+// Split-K ranges of few, deep output tiles: 128 x 128 tiles, 4 waves of 64 x 64, two
+// 64-deep stages (64 KB of LDS, two workgroups per CU); float partials, summed below.
+__global__ __launch_bounds__(256, 2) void gemm_lds_splitk_kernel(GemmArgs p, int nb1, int nmb,
+                                                                 int total) {
+  gemm_lds_body<128, 128, 2, 2, 2, true>(p, nb1, nmb, total);
+}
+
+// Y[m][n] = bf16(sum over ranges of part[r][m][n]), four columns per thread.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* part, int splits,
+                                                                 int64_t mn4, int64_t mn,
+                                                                 bf16* y) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < mn4; i += (int64_t)gridDim.x * 256) {
+    f32x4 acc = *(const f32x4*)(part + 4 * i);
+    for (int r = 1; r < splits; ++r) {
+      const f32x4 v = *(const f32x4*)(part + (int64_t)r * mn + 4 * i);
+      acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+    }
+    u32x2 w;
+    w[0] = pack_bf16x2(acc[0], acc[1]);
+    w[1] = pack_bf16x2(acc[2], acc[3]);
+    *(u32x2*)(y + 4 * i) = w;
+  }
+}
+
 template <int BM, int BN, int NT>
 hipError_t launch_cfg(void (*kernel)(GemmArgs, int, int, int), const GemmArgs& p,
                       hipStream_t s) {
@@ -366,6 +421,40 @@ hipError_t launch_gemm_lds(const GemmArgs& p, hipStream_t s) {
                    ((p.N + 191) / 192 + (p.w2 ? (p.N2 + 191) / 192 : 0));
   if (big >= 512) return launch_cfg<256, 192, 512>(gemm_lds_wide_kernel, p, s);
   return launch_cfg<64, 64, 256>(gemm_lds_narrow_kernel, p, s);
+}
+
+void gemm_splitk_plan(int M, int N, int K, int* splits, int* kps) {
+  *splits = 1;
+  *kps = K / BK;
+  if (M <= 0 || N <= 0 || K % BK || N % 8) return;
+  const long tiles = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const int nk = K / BK;
+  // only products whose output alone cannot fill the 256 CUs twice, and at least eight
+  // 64-deep stages per range
+  if (tiles >= 256 || nk < 16) return;
+  long s = (512 + tiles - 1) / tiles;
+  if (s > nk / 8) s = nk / 8;
+  if (s < 2) return;
+  const int k = (int)((nk + s - 1) / s);
+  *kps = k;
+  *splits = (nk + k - 1) / k;
+}
+
+hipError_t launch_gemm_splitk(const GemmArgs& p, hipStream_t s) {
+  const int nmb = (p.M + 127) / 128;
+  const int nb1 = (p.N + 127) / 128;
+  const long total = (long)nmb * nb1 * p.splits;
+  if (total > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(gemm_lds_splitk_kernel, dim3((unsigned)total), dim3(256), 0, s, p, nb1, nmb,
+                     (int)total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t mn = (int64_t)p.M * p.N;
+  int64_t blocks = (mn / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.part,
+                     p.splits, mn / 4, mn, (bf16*)p.y);
+  return hipGetLastError();
 }
 
 }  // namespace gmla

@@ -600,3 +600,45 @@ int gmla_linear(int dtype, int M, int N, int K, const void* X, const void* W, vo
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t gmla_linear_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  int splits, kps;
+  gemm_splitk_plan(M, N, K, &splits, &kps);
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+}
+
+int gmla_linear_ws(int dtype, int M, int N, int K, const void* X, const void* W, void* Y,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || M <= 0 || N <= 0 || K <= 0) return GMLA_ERR_INVALID_ARG;
+  if (!X || !W || !Y) return GMLA_ERR_INVALID_ARG;
+  const size_t es = elem_size(dtype);
+  if (!aligned(X, es) || !aligned(W, es) || !aligned(Y, es)) return GMLA_ERR_INVALID_ARG;
+  if (dtype == GMLA_BF16 && (K % 8 || !aligned(X, 16) || !aligned(W, 16)))
+    return GMLA_ERR_INVALID_ARG;
+  GemmArgs p;
+  p.M = M; p.N = N; p.K = K;
+  p.x = X; p.w = W; p.w2 = nullptr; p.N2 = 0;
+  p.g = nullptr; p.y = Y; p.y2 = nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  int splits = 1, kps = 0;
+  if (dtype == GMLA_BF16) gemm_splitk_plan(M, N, K, &splits, &kps);
+  const size_t need = (size_t)splits * M * N * sizeof(float);
+  // the split path needs 16-byte rows everywhere and the partials' space; otherwise the
+  // call is gmla_linear
+  if (splits > 1 && workspace && workspace_bytes >= need && aligned(workspace, 16) &&
+      aligned(Y, 16) && (int64_t)128 * K * 2 < ((int64_t)1 << 31)) {
+    p.part = (float*)workspace;
+    p.splits = splits;
+    p.kps = kps;
+    if (log_enabled())
+      fprintf(stderr, "gmla: linear split-K M=%d N=%d K=%d ranges=%d (%d stages each)\n", M, N, K,
+              splits, kps);
+    return hip_status(launch_gemm_splitk(p, s));
+  }
+  return hip_status(launch_gemm(dtype, p, s));
+}
+
+}  // extern "C"

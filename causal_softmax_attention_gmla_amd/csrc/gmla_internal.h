@@ -145,12 +145,21 @@ struct GemmArgs {
   const void* g;   // nullable gate logits [M, K]: A operand = sigmoid(g) * x
   void* y;         // [M, N]
   void* y2;        // [M, N2] or NULL
+  // split-K: the k stages are dealt to `splits` ranges of `kps` stages; each writes float
+  // partials part[split][M][N], summed by a second kernel (NULL: no split)
+  float* part = nullptr;
+  int splits = 1;
+  int kps = 0;
 };
 hipError_t launch_gemm(int dtype, const GemmArgs& a, hipStream_t s);
 // LDS-direct pipelined bf16 GEMM: no gate, K a multiple of 64, N (and N2) a multiple
 // of 8, 16-byte aligned operands, 8-byte aligned outputs.
 bool gemm_lds_supported(const GemmArgs& a);
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
+// Split-K plan for a bf16 product with few output tiles and a deep K: the number of
+// ranges (1: no split) and the stages (of 64) per range.
+void gemm_splitk_plan(int M, int N, int K, int* splits, int* kps);
+hipError_t launch_gemm_splitk(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gate_only(int dtype, int64_t n, const void* g, const void* x, void* y,
                             hipStream_t s);
 

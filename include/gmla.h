@@ -286,6 +286,20 @@ int gmla_gate_out(int dtype, int M, int d_model, const void* G, const void* O_ti
 int gmla_linear(int dtype, int M, int N, int K, const void* X, const void* W, void* Y,
                 void* stream);
 
+/*
+ * gmla_linear with a caller workspace for products with few output tiles and a deep
+ * reduction (the latent down-projection C = X W_c^T: 2048 x 512 x 12288): the reduction
+ * is split into ranges computed in parallel into float partials in the workspace, then
+ * summed and rounded to bf16 (a sum in another order than gmla_linear's, to float
+ * rounding).  gmla_linear_workspace_bytes(M, N, K) is the space that path needs, 0 when
+ * the shape does not use it; with a smaller or NULL workspace (or fp32) the call is
+ * exactly gmla_linear.  The workspace (16-byte aligned) is owned by the caller and not
+ * shared with a concurrent call.
+ */
+size_t gmla_linear_workspace_bytes(int M, int N, int K);
+int gmla_linear_ws(int dtype, int M, int N, int K, const void* X, const void* W, void* Y,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

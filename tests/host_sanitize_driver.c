@@ -99,6 +99,9 @@ int main(void) {
   EXPECT(gmla_linear(GMLA_BF16, 64, 64, 64, F, F, F, 0), GMLA_ERR_HIP);
   EXPECT(gmla_linear(GMLA_BF16, 2048, 12288, 128, F, F, F, 0), GMLA_ERR_HIP);
   EXPECT(gmla_linear(GMLA_F32, 3, 5, 7, F, F, F, 0), GMLA_ERR_HIP);
+  if (gmla_linear_workspace_bytes(2048, 512, 12288) != (size_t)8 * 2048 * 512 * 4) ++failures;
+  EXPECT(gmla_linear_ws(GMLA_BF16, 2048, 512, 12288, F, F, F, F, (size_t)1 << 26, 0), GMLA_ERR_HIP);
+  EXPECT(gmla_linear_ws(GMLA_BF16, 4, 4, 12, F, F, F, F, 0, 0), GMLA_ERR_INVALID_ARG);
   EXPECT(gmla_latent_expand(GMLA_BF16, 4, 8, 16, F, 0, F, F, F, 0), GMLA_ERR_INVALID_ARG);
   EXPECT(gmla_latent_expand(GMLA_BF16, 64, 64, 128, F, F, F, F, F, 0), GMLA_ERR_HIP);
   EXPECT(gmla_gate_out(GMLA_BF16, 4, 16, 0, 0, 0, F, 0), GMLA_ERR_INVALID_ARG);

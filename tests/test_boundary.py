@@ -306,6 +306,18 @@ def test_projection_argument_checks():
     assert lib.gmla_gate_out(3, 4, 16, None, FAKE, None, FAKE, None) == -1
 
 
+def test_linear_split_k_plan_and_arguments():
+    lib = gm.library()
+    # the latent down-projection splits its 12288-deep reduction; wide or shallow products do not
+    assert lib.gmla_linear_workspace_bytes(2048, 512, 12288) == 8 * 2048 * 512 * 4
+    assert lib.gmla_linear_workspace_bytes(2048, 12288, 12288) == 0
+    assert lib.gmla_linear_workspace_bytes(2048, 24576, 512) == 0
+    assert lib.gmla_linear_workspace_bytes(2048, 512, 512) == 0
+    assert lib.gmla_linear_ws(1, 4, 4, 12, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.gmla_linear_ws(1, 0, 4, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.gmla_linear_ws(3, 4, 4, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+
+
 def test_binding_rejects_cpu_tensors_and_mismatches():
     import torch
     q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
@@ -361,6 +373,8 @@ def valid_calls_without_a_device():
     assert _noalloc(splits=4) == -4  # the scratch lookup fails without a device
     assert _latent() == -4
     assert _platent() == -4
+    assert lib.gmla_linear_ws(1, 2048, 512, 12288, FAKE, FAKE, FAKE, FAKE, 1 << 26, None) == -4
+    assert lib.gmla_linear_ws(1, 64, 64, 64, FAKE, FAKE, FAKE, None, 0, None) == -4
     assert _varlen() == -4
     assert _varlen(dtype=0, D=64) == -4
     assert _decode_varlen() == -4

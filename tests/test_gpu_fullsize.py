@@ -88,6 +88,19 @@ def test_prefill_offsets_past_2_31_sampled():
     del qkv, out
 
 
+def test_latent_down_projection_split_k_every_row():
+    """The layer's latent down-projection C = X W_c^T (2048 x 512 x 12288) on the split-K
+    path: every row against the oracle."""
+    dev = need_gpu()
+    announce("linear split-K 2048x512x12288, every row")
+    x, ws = I.workload_inputs("layer_t2048", dev)
+    x2 = x.view(-1, x.shape[-1])
+    assert gm.library().gmla_linear_workspace_bytes(2048, 512, 12288) > 0
+    c = gm.linear(x2, ws["Wc"])
+    torch.cuda.synchronize()
+    check_rows_rel(host(c), oracle.linear(host(x2), host(ws["Wc"])), 512)
+
+
 def test_linear_offsets_past_2_31_sampled():
     """Y = X W^T with X [300000, 8192] (2.46e9 elements, past 32-bit element offsets) on
     the 256 x 384-tile kernel; every output written, sampled rows (the last ones beyond

@@ -749,3 +749,30 @@ def test_gated_mla_layer_fused_latent(causal):
     check_rows_rel(host(res["output"]), ref["output"], dm)
     assert torch.equal(res["latent_cache"], two["latent_cache"])
     assert torch.equal(res["output"], two["output"])
+
+
+# ---------------------------------------------------------------- split-K projection
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 264, 4096), (1, 8, 8192), (130, 136, 2048), (2000, 520, 6144)])
+def test_linear_split_k(M, N, K):
+    """Products with few output tiles and a deep K take the split-K path (float partials
+    in a workspace, then a summing kernel): every row against the oracle, and the output
+    written inside its buffer only (NaN guard band around it)."""
+    dev = need_gpu()
+    lib = gm.library()
+    assert lib.gmla_linear_workspace_bytes(M, N, K) > 0
+    announce(f"linear split-K {M}x{N}x{K}")
+    x = I.normal((M, K), torch.bfloat16, dev, seed=9400 + K)
+    w = I.normal((N, K), torch.bfloat16, dev, seed=9401 + K, std=K ** -0.5)
+    buf = torch.full((M * N + 2048,), float("nan"), dtype=torch.bfloat16, device=dev)
+    y = buf[1024:1024 + M * N].view(M, N)
+    gm.linear(x, w, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any()
+    assert torch.isnan(buf[:1024]).all() and torch.isnan(buf[1024 + M * N:]).all()
+    check_rows_rel(host(y), oracle.linear(host(x), host(w)), N)
+    # without the workspace the same call runs the single-pass kernels
+    z = gm.linear(x, w, split_k=False)
+    torch.cuda.synchronize()
+    check_rows_rel(host(z), host(y), N)
