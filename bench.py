@@ -50,6 +50,8 @@ KERNEL_SOURCES = {
                             "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"],
     "decode_split_kernel": ["causal_softmax_attention_gmla_amd/csrc/decode.hip",
                             "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"],
+    "latent_split_kernel_512": ["causal_softmax_attention_gmla_amd/csrc/decode_latent.hip",
+                                "causal_softmax_attention_gmla_amd/csrc/gmla_internal.h"],
 }
 
 
@@ -426,7 +428,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--only", choices=["prefill", "decode", "layer", "decode_long", "decode_latent",
-                                       "copy"])
+                                       "gate_out", "copy"])
     ap.add_argument("--summarize-stats", metavar="DIR")
     ap.add_argument("--timed-window", nargs=2, type=int, metavar=("W", "K"),
                     help="with --summarize-stats: also average dispatches W .. W+K-1 per kernel")
@@ -540,8 +542,25 @@ def main():
             result.update({"value": round(gbps, 1), "unit": "GB/s",
                            "ms_per_step": round(dwall * 1e3 / dcalls, 4)})
 
-    if args.all or only in ("layer", "decode_long", "decode_latent"):
+    if args.all or only in ("layer", "decode_long", "decode_latent", "gate_out"):
         extra = {}
+        if only == "gate_out":
+            # the output projection with the gate applied in the GEMM prologue (one launch
+            # of the register-staged kernel) against the gate applied by its own kernel and
+            # the LDS-pipelined GEMM (two launches), at the layer's shape
+            M_, dm_ = 2048, 12288
+            o_ = I.normal((M_, dm_), torch.bfloat16, dev, seed=7201)
+            g_ = I.normal((M_, dm_), torch.bfloat16, dev, seed=7202)
+            w_ = I.normal((dm_, dm_), torch.bfloat16, dev, seed=7203, std=dm_ ** -0.5)
+            gflop = 2 * M_ * dm_ * dm_
+            a1, _, _ = time_calls(torch, lambda i: gm.gate_out(o_, w_, g_), max(5, K // 5), max(2, W // 3))
+            a2, _, _ = time_calls(torch, lambda i: gm.linear(gm.gate_out(o_, None, g_), w_),
+                                  max(5, K // 5), max(2, W // 3))
+            extra["gate_out_t2048"] = {
+                "prologue_gate_ms": round(a1, 4), "prologue_gate_tflops": round(gflop / (a1 * 1e-3) / 1e12, 1),
+                "separate_gate_ms": round(a2, 4), "separate_gate_tflops": round(gflop / (a2 * 1e-3) / 1e12, 1),
+                "algorithmic_flop": gflop}
+            del o_, g_, w_
         if only in (None, "layer"):
             lw = I.WORKLOADS["layer_t2048"]
             ld = lw.dims
