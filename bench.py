@@ -121,6 +121,23 @@ def time_calls(torch, fn, steps, warmup, rotate=1):
     return region / steps, fastest, wall
 
 
+def settle(torch, fn, seconds):
+    """Call fn back to back for about `seconds`, untimed.  From idle, a GPU's first few
+    dozen calls of sustained matrix-core work run up to 30% slower than the rest while its
+    power management brings the clock from the idle boost down to the sustained level and
+    back up (traced per dispatch: 804, 919, 1055, ... 790 us for the prefill workload);
+    this puts the timed calls after that transient.  Returns the number of calls."""
+    if seconds <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn(0)
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
 def loop_calls(torch, fn, seconds, work, unit):
     """Call fn back to back for about `seconds`, printing the rate of each 20-call batch
     every half second (for sampling clocks or power from another process meanwhile)."""
@@ -424,6 +441,8 @@ def main():
     # A fresh GPU runs the first few dozen prefill calls up to 30% slower while its clocks
     # settle under sustained matrix-core load; 60 untimed calls reach the steady state.
     ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed prefill calls before the warm-up (0: none)")
     ap.add_argument("--all", action="store_true", help="also time the layer, the 131072-key decode and the latent-cache decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-splits", type=int, default=0)
@@ -492,12 +511,16 @@ def main():
         if args.loop:
             return loop_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), args.loop,
                               flops, "TFLOP/s")
+        settle_calls = settle(torch, lambda i: gm.attend_prefill(q, k, v, out=out), args.settle)
         avg, fastest, wall = time_calls(torch, lambda i: gm.attend_prefill(q, k, v, out=out), K, W)
         tflops = flops / (avg * 1e-3) / 1e12
         result.update({
             "value": round(tflops, 2), "ms_per_step": round(wall * 1e3 / K, 4),
             "config": {"workload": pw.name, "B": d["B"], "T": d["T"], "H": d["H"], "D": d["D"],
                        "causal": True, "inputs": "N(0,1) rounded to bf16, seeded"},
+            "clock_settle": {"seconds": args.settle, "calls": settle_calls,
+                             "note": "untimed back-to-back calls before the warm-up, so that the "
+                                     "timed calls run at the sustained clock"},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": measured_traffic("prefill_bf16_kernel"),
@@ -553,9 +576,9 @@ def main():
             g_ = I.normal((M_, dm_), torch.bfloat16, dev, seed=7202)
             w_ = I.normal((dm_, dm_), torch.bfloat16, dev, seed=7203, std=dm_ ** -0.5)
             gflop = 2 * M_ * dm_ * dm_
-            a1, _, _ = time_calls(torch, lambda i: gm.gate_out(o_, w_, g_), max(5, K // 5), max(2, W // 3))
-            a2, _, _ = time_calls(torch, lambda i: gm.linear(gm.gate_out(o_, None, g_), w_),
+            a1, _, _ = time_calls(torch, lambda i: gm.gate_out(o_, w_, g_, fused_gate=True),
                                   max(5, K // 5), max(2, W // 3))
+            a2, _, _ = time_calls(torch, lambda i: gm.gate_out(o_, w_, g_), max(5, K // 5), max(2, W // 3))
             extra["gate_out_t2048"] = {
                 "prologue_gate_ms": round(a1, 4), "prologue_gate_tflops": round(gflop / (a1 * 1e-3) / 1e12, 1),
                 "separate_gate_ms": round(a2, 4), "separate_gate_tflops": round(gflop / (a2 * 1e-3) / 1e12, 1),

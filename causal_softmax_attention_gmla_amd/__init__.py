@@ -441,8 +441,13 @@ def latent_expand(c: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, *, stre
 
 
 def gate_out(o_tilde: torch.Tensor, w_o: torch.Tensor | None = None, gate: torch.Tensor | None = None,
-             *, stream=None) -> torch.Tensor:
-    """Y = [sigmoid(gate) * O~] W_o^T (gate before the projection); either part optional."""
+             *, fused_gate: bool = False, stream=None) -> torch.Tensor:
+    """Y = [sigmoid(gate) * O~] W_o^T (gate before the projection); either part optional.
+
+    With both parts in bf16 the gate runs as its own pass into a workspace allocated here
+    and the projection on the LDS-pipelined GEMM (gmla_gate_out_ws); fused_gate=True
+    applies the gate inside the GEMM's tile staging instead (gmla_gate_out, no workspace,
+    about 4x slower at the layer's shape)."""
     d_model = o_tilde.shape[-1]
     if gate is not None and gate.shape != o_tilde.shape:
         raise ValueError("gate must have O~'s shape")
@@ -455,8 +460,16 @@ def gate_out(o_tilde: torch.Tensor, w_o: torch.Tensor | None = None, gate: torch
     _same_dtype(o_tilde, w_o, gate)
     M = o_tilde.numel() // d_model
     Y = torch.empty_like(o_tilde)
-    st = _lib.load().gmla_gate_out(_dtype(o_tilde), M, d_model, _ptr(gate), _ptr(o_tilde), _ptr(w_o),
-                                   _ptr(Y), _stream(dev, stream))
+    lib = _lib.load()
+    nws = lib.gmla_gate_out_workspace_bytes(_dtype(o_tilde), M, d_model)
+    if gate is not None and w_o is not None and nws and not fused_gate:
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        st = lib.gmla_gate_out_ws(_dtype(o_tilde), M, d_model, _ptr(gate), _ptr(o_tilde), _ptr(w_o),
+                                  _ptr(Y), _ptr(ws), nws, _stream(dev, stream))
+        _lib.check(st, "gmla_gate_out_ws")
+        return Y
+    st = lib.gmla_gate_out(_dtype(o_tilde), M, d_model, _ptr(gate), _ptr(o_tilde), _ptr(w_o),
+                           _ptr(Y), _stream(dev, stream))
     _lib.check(st, "gmla_gate_out")
     return Y
 

@@ -49,6 +49,8 @@ SIGNATURES = {
                                         _vp]),
     "gmla_latent_expand": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "gmla_gate_out": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "gmla_gate_out_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
+    "gmla_gate_out_ws": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "gmla_linear": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "gmla_linear_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i]),
     "gmla_linear_ws": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <utility>
 
 #include "gmla_internal.h"
 
@@ -639,6 +640,43 @@ int gmla_linear_ws(int dtype, int M, int N, int K, const void* X, const void* W,
     return hip_status(launch_gemm_splitk(p, s));
   }
   return hip_status(launch_gemm(dtype, p, s));
+}
+
+// The gated bf16 projection through the LDS-pipelined GEMM: the gate kernel writes
+// sigmoid(G) (.) O~ (rounded to bf16, exactly the operand the gate prologue forms) to the
+// workspace, which is then the GEMM's A operand.  Zero when the shape does not take it.
+size_t gmla_gate_out_workspace_bytes(int dtype, int M, int d_model) {
+  if (dtype != GMLA_BF16 || M <= 0 || d_model <= 0 || d_model % 64) return 0;
+  if ((int64_t)256 * d_model * 2 >= ((int64_t)1 << 31)) return 0;
+  return (size_t)M * d_model * 2;
+}
+
+int gmla_gate_out_ws(int dtype, int M, int d_model, const void* G, const void* O_tilde,
+                     const void* W_o, void* Y, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const size_t need = gmla_gate_out_workspace_bytes(dtype, M, d_model);
+  if (!G || !W_o || need == 0 || !workspace || workspace_bytes < need ||
+      !aligned(workspace, 16) || !O_tilde || !Y || !aligned(O_tilde, 16) || !aligned(G, 16) ||
+      !aligned(W_o, 16) || !aligned(Y, 16))
+    return gmla_gate_out(dtype, M, d_model, G, O_tilde, W_o, Y, stream);
+  // the workspace may not overlap an input or the output (it is written while they are read)
+  const auto span = [](const void* p, size_t n) {
+    return std::make_pair((uintptr_t)p, (uintptr_t)p + n);
+  };
+  const auto ws = span(workspace, need);
+  const size_t mat = (size_t)M * d_model * 2;
+  for (auto o : {span(G, mat), span(O_tilde, mat), span(W_o, (size_t)d_model * d_model * 2),
+                 span(Y, mat)})
+    if (ws.first < o.second && o.first < ws.second) return GMLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs p;
+  p.M = M; p.N = d_model; p.K = d_model;
+  p.x = workspace; p.w = W_o; p.w2 = nullptr; p.N2 = 0;
+  p.g = nullptr; p.y = Y; p.y2 = nullptr;
+  if (!gemm_lds_supported(p)) return gmla_gate_out(dtype, M, d_model, G, O_tilde, W_o, Y, stream);
+  const hipError_t e = launch_gate_only(dtype, (int64_t)M * d_model, G, O_tilde, workspace, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_gemm_lds(p, s));
 }
 
 }  // extern "C"

@@ -306,6 +306,25 @@ def test_projection_argument_checks():
     assert lib.gmla_gate_out(3, 4, 16, None, FAKE, None, FAKE, None) == -1
 
 
+def test_gate_out_workspace_size_and_overlap():
+    lib = gm.library()
+    # bf16 with d_model a multiple of 64 takes the gate pass + LDS GEMM; others need nothing
+    assert lib.gmla_gate_out_workspace_bytes(1, 2048, 12288) == 2048 * 12288 * 2
+    assert lib.gmla_gate_out_workspace_bytes(1, 3, 64) == 3 * 64 * 2
+    assert lib.gmla_gate_out_workspace_bytes(0, 2048, 12288) == 0
+    assert lib.gmla_gate_out_workspace_bytes(1, 2048, 100) == 0
+    assert lib.gmla_gate_out_workspace_bytes(1, 0, 128) == 0
+    # a workspace overlapping an operand is rejected before anything launches
+    M, dm = 64, 128
+    mat = M * dm * 2
+    G, O, W, Y = (ctypes.c_void_p((1 << 24) * (i + 1)) for i in range(4))
+    for start in (G.value - 16, O.value + mat - 16, W.value, Y.value + 4096):
+        ws = ctypes.c_void_p(start)
+        assert lib.gmla_gate_out_ws(1, M, dm, G, O, W, Y, ws, mat, None) == -1, hex(start)
+    # invalid arguments are still caught with a workspace
+    assert lib.gmla_gate_out_ws(1, 4, 16, None, None, None, FAKE, FAKE, 1 << 20, None) == -1
+
+
 def test_linear_split_k_plan_and_arguments():
     lib = gm.library()
     # the latent down-projection splits its 12288-deep reduction; wide or shallow products do not
@@ -381,6 +400,8 @@ def valid_calls_without_a_device():
     assert lib.gmla_linear(1, 64, 64, 64, FAKE, FAKE, FAKE, None) == -4
     assert lib.gmla_latent_expand(1, 64, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -4
     assert lib.gmla_gate_out(1, 64, 128, FAKE, FAKE, FAKE, FAKE, None) == -4
+    ws = ctypes.c_void_p(1 << 30)
+    assert lib.gmla_gate_out_ws(1, 64, 128, FAKE, FAKE, FAKE, FAKE, ws, 64 * 128 * 2, None) == -4
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path only")

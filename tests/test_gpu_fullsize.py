@@ -101,6 +101,29 @@ def test_latent_down_projection_split_k_every_row():
     check_rows_rel(host(c), oracle.linear(host(x2), host(ws["Wc"])), 512)
 
 
+def test_gate_out_t2048_both_routes_sampled():
+    """The gated output projection at the layer's shape (M = 2048, d_model = 12288, bf16),
+    both routes: gate pass + LDS GEMM and gate in the GEMM's tile staging.  64 rows over
+    every 256-row tile against the oracle, and the two routes within the same bound of
+    each other everywhere."""
+    dev = need_gpu()
+    announce("gate_out 2048x12288 both routes, 64 rows")
+    M, dm = 2048, 12288
+    o = I.normal((M, dm), torch.bfloat16, dev, seed=7201)
+    g = I.normal((M, dm), torch.bfloat16, dev, seed=7202)
+    w = I.normal((dm, dm), torch.bfloat16, dev, seed=7203, std=dm ** -0.5)
+    assert gm.library().gmla_gate_out_workspace_bytes(1, M, dm) == M * dm * 2
+    y_ws = gm.gate_out(o, w, g)
+    y_fu = gm.gate_out(o, w, g, fused_gate=True)
+    torch.cuda.synchronize()
+    rows = layer_rows()
+    ref = oracle.linear(oracle.gate(host(g[rows]), host(o[rows])), host(w))
+    check_rows_rel(host(y_ws[rows]), ref, dm)
+    check_rows_rel(host(y_fu[rows]), ref, dm)
+    check_rows_rel(host(y_ws), host(y_fu), dm)
+    del o, g, w, y_ws, y_fu
+
+
 def test_linear_offsets_past_2_31_sampled():
     """Y = X W^T with X [300000, 8192] (2.46e9 elements, past 32-bit element offsets) on
     the 256 x 384-tile kernel; every output written, sampled rows (the last ones beyond

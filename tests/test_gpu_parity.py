@@ -449,15 +449,18 @@ def test_latent_expand(dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("with_gate,with_proj", [(True, True), (True, False), (False, True)])
-def test_gate_out(dtype, with_gate, with_proj):
+@pytest.mark.parametrize("with_gate,with_proj,fused_gate", [(True, True, False), (True, True, True),
+                                                            (True, False, False), (False, True, False)])
+@pytest.mark.parametrize("M,dm", [(96, 256), (333, 320)])
+def test_gate_out(dtype, with_gate, with_proj, fused_gate, M, dm):
+    """Both routes of the gated projection (gate pass into a workspace + LDS GEMM, and the
+    gate in the GEMM's tile staging), with a row count that leaves a ragged tile."""
     dev = need_gpu()
-    announce(f"gate_out {dtype} gate={with_gate} proj={with_proj}")
-    M, dm = 96, 256
+    announce(f"gate_out {dtype} gate={with_gate} proj={with_proj} fused={fused_gate} M={M} dm={dm}")
     o = I.normal((M, dm), dtype, dev, seed=4200)
     g = I.normal((M, dm), dtype, dev, seed=4201) if with_gate else None
     w = I.normal((dm, dm), dtype, dev, seed=4202, std=dm ** -0.5) if with_proj else None
-    y = gm.gate_out(o, w, g)
+    y = gm.gate_out(o, w, g, fused_gate=fused_gate)
     torch.cuda.synchronize()
     ref = host(o)
     if with_gate:
@@ -468,6 +471,27 @@ def test_gate_out(dtype, with_gate, with_proj):
         check_f32_abs(host(y), ref)
     else:
         check_rows_rel(host(y), ref, dm)
+
+
+def test_gate_only_unaligned_rows_match_aligned():
+    """The bf16 gate pass takes 8 elements per lane when every pointer is 16-byte aligned
+    and one element per lane otherwise; both round the same float to bf16."""
+    dev = need_gpu()
+    announce("gate only, aligned vs 2-byte offset views")
+    M, dm = 37, 264
+    ob = I.normal((M * dm + 1,), torch.bfloat16, dev, seed=4210)
+    gb = I.normal((M * dm + 1,), torch.bfloat16, dev, seed=4211)
+    y_al = gm.gate_out(ob[:-1].view(M, dm), None, gb[:-1].view(M, dm))
+    o_un, g_un = ob[:-1].clone(), gb[:-1].clone()
+    buf_o = torch.empty(M * dm + 1, dtype=torch.bfloat16, device=dev)
+    buf_g = torch.empty(M * dm + 1, dtype=torch.bfloat16, device=dev)
+    buf_o[1:] = o_un
+    buf_g[1:] = g_un
+    y_un = gm.gate_out(buf_o[1:].view(M, dm), None, buf_g[1:].view(M, dm))
+    torch.cuda.synchronize()
+    assert torch.equal(y_al, y_un)
+    ref = oracle.gate(host(gb[:-1].view(M, dm)), host(ob[:-1].view(M, dm)))
+    check_rows_rel(host(y_al), ref, dm)
 
 
 def test_gate_example_on_gpu():
