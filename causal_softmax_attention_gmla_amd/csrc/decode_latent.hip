@@ -14,7 +14,8 @@
 // read are the d_c latent values (shared by all heads) instead of H * 256 key and value
 // values.  Three launches:
 //  1. absorb:  q'[b, h, :] = scale * log2(e) * W_k,h^T q[b, h, :]  (bf16, workspace);
-//  2. split:   grid (split, 32-head block, batch).  The workgroup's key range is walked
+//  2. split:   one workgroup per (key range, 32-head block, batch row), the head blocks
+//     of a (range, row) pair on one XCD.  The workgroup's key range is walked
 //     in tiles of 32 latent rows staged in LDS (buffer loads in the LDS-direct form, one
 //     tile ahead; rows past N load as zeros).  Wave w owns latent channels
 //     [w d_c / 4, (w + 1) d_c / 4): it forms its share of the scores S^T = C q'^T
@@ -159,7 +160,14 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
   constexpr int LPW = KT / RPI / 4;  // load instructions per wave per tile
   static_assert(DC % 128 == 0 && DC <= kMaxDc, "latent width");
 
-  const int split = blockIdx.x, hb = blockIdx.y, b = blockIdx.z;
+  // Grid (8 nhb, npy, npz): workgroup (x + 8 hb, g) takes head block hb of range pair
+  // p = 8 g + x, i.e. (split p mod splits, batch row p / splits).  Workgroups are dealt to
+  // the XCDs round-robin in launch order, so the nhb head blocks of one pair run on the
+  // same XCD and read its latent rows through the same L2.
+  const int hb = blockIdx.x >> 3;
+  const int pair = 8 * (blockIdx.y + gridDim.y * blockIdx.z) + (blockIdx.x & 7);
+  if (pair >= a.splits * a.B) return;
+  const int split = pair % a.splits, b = pair / a.splits;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -347,7 +355,8 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
 }
 
 // ---------------------------------------------------------------- 3. merge, W_v, gate
-// grid (128 / 32, H, ceil(B / kMergeRows)); thread t: output channel d = d0 + t / 8; part
+// One workgroup per (head, 32 output channels, kMergeRows batch rows), all of a head's on
+// one XCD; thread t: output channel d = d0 + t / 8; part
 // p = t mod 8 takes latent channels 64 i + 8 p .. +7 (i = 0 .. DC/64 - 1) of the W_v row.
 // For its batch rows the workgroup first turns each row's split maxima into merge weights
 // f_j = 2^(m_j - m) and 1 / l in LDS (one wave per row), then merges u for all its rows
@@ -361,12 +370,19 @@ __global__ __launch_bounds__(NT) void latent_merge_kernel(LatentDecodeArgs a) {
   __shared__ float fw[kMergeRows][kMaxMergeSplits];
   __shared__ float inv_l[kMergeRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.y;
-  const int b0 = blockIdx.z * kMergeRows;
+  // Grid (8 G, ceil(H / 8)) with G = 4 ceil(B / kMergeRows) workgroups per head: workgroup
+  // (x + 8 r, y) takes head 8 y + x, channel block r mod 4 and the batch rows of block r / 4.
+  // Dealt to the XCDs round-robin in launch order, all G workgroups of a head run on one
+  // XCD, so its W_v rows and split partials are read from HBM once and then from L2.
+  const int slot = blockIdx.x >> 3;
+  const int h = 8 * blockIdx.y + (blockIdx.x & 7);
+  if (h >= a.H) return;
+  const int cb = slot & 3;
+  const int b0 = (slot >> 2) * kMergeRows;
   const int nb = min(kMergeRows, a.B - b0);
   const int S = a.splits;
   // this thread's W_v values (issued first: their latency overlaps the merge)
-  const int d = blockIdx.x * 32 + (tid >> 3);
+  const int d = cb * 32 + (tid >> 3);
   const int p = tid & 7;
   u32x4 wv[NI];
   {
@@ -470,12 +486,15 @@ hipError_t launch_latent_t(void (*split_kernel)(LatentDecodeArgs), const LatentD
   hipLaunchKernelGGL((latent_absorb_kernel<DC>), dim3(DC / 64, a.H), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(split_kernel, dim3(a.splits, (a.H + HB - 1) / HB, a.B), dim3(NT),
-                     0, s, a);
+  const int nhb = (a.H + HB - 1) / HB;
+  const long pg = ((long)a.splits * a.B + 7) / 8;  // groups of 8 range pairs
+  const long npy = pg < 32768 ? pg : 32768;
+  const long npz = (pg + npy - 1) / npy;
+  hipLaunchKernelGGL(split_kernel, dim3(8 * nhb, (unsigned)npy, (unsigned)npz), dim3(NT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((latent_merge_kernel<DC>),
-                     dim3(LHD / 32, a.H, (a.B + kMergeRows - 1) / kMergeRows), dim3(NT), 0, s, a);
+  const int G = 4 * ((a.B + kMergeRows - 1) / kMergeRows);
+  hipLaunchKernelGGL((latent_merge_kernel<DC>), dim3(8 * G, (a.H + 7) / 8), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
