@@ -16,8 +16,8 @@
 //  1. absorb:  q'[b, h, :] = scale * log2(e) * W_k,h^T q[b, h, :]  (bf16, workspace);
 //  2. split:   one workgroup per (key range, 32-head block, batch row), the head blocks
 //     of a (range, row) pair on one XCD.  The workgroup's key range is walked
-//     in tiles of 32 latent rows staged in LDS (buffer loads in the LDS-direct form, one
-//     tile ahead; rows past N load as zeros).  Wave w owns latent channels
+//     in tiles of 32 latent rows staged in LDS (buffer loads in the LDS-direct form, three
+//     tiles ahead; rows past N load as zeros).  Wave w owns latent channels
 //     [w d_c / 4, (w + 1) d_c / 4): it forms its share of the scores S^T = C q'^T
 //     (v_mfma_f32_32x32x16_bf16, keys x heads), the four shares are summed through LDS in
 //     a fixed order (every wave then holds the same scores), the online softmax runs in
@@ -48,15 +48,18 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
 // One array per buffer, so the compiler can tell a load into one from reads of another.
-// Three tile buffers: tile j + 2 is requested while tile j is used.
+// Four tile buffers: tile j + 3 is requested while tile j is used, so three tiles' loads
+// (96 KB at d_c = 512) are in flight per workgroup while it computes: a step then waits for
+// a third of the memory latency rather than half.
 __shared__ __align__(16) bf16 lat_c0[KT * kMaxDc];
 __shared__ __align__(16) bf16 lat_c1[KT * kMaxDc];
 __shared__ __align__(16) bf16 lat_c2[KT * kMaxDc];
+__shared__ __align__(16) bf16 lat_c3[KT * kMaxDc];
 // score shares [wave][quad][lane]: written after a tile's first barrier and read after its
 // second, so the next tile's first barrier already separates the reads from the rewrite
 __shared__ __align__(16) f32x4 lat_x[4 * 4 * 64];
 template <int P> __device__ __forceinline__ bf16* cbuf() {
-  return P == 0 ? lat_c0 : P == 1 ? lat_c1 : lat_c2;
+  return P == 0 ? lat_c0 : P == 1 ? lat_c1 : P == 2 ? lat_c2 : lat_c3;
 }
 
 // s_waitcnt vmcnt(N) (N < 64) leaving the other counters alone.
@@ -246,13 +249,15 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
 
   auto step = [&](int tile, auto parity) __attribute__((always_inline)) {
     constexpr int P = decltype(parity)::value;
-    // this wave's loads of the tile are done when at most the next tile's are in flight
-    if (tile + 1 < t_last)
+    // this wave's loads of the tile are done when at most the next two tiles' are in flight
+    if (tile + 2 < t_last)
+      wait_vmcnt<2 * LPW>();
+    else if (tile + 1 < t_last)
       wait_vmcnt<LPW>();
     else
       wait_vmcnt<0>();
-    lds_barrier();  // tile in LDS; every wave is done with tile - 1 and the shares
-    if (tile + 2 < t_last) load_tile(tile + 2, std::integral_constant<int, (P + 2) % 3>{});
+    lds_barrier();  // tile in LDS; every wave is done with tile - 1 (whose buffer is refilled)
+    if (tile + 3 < t_last) load_tile(tile + 3, std::integral_constant<int, (P + 3) % 4>{});
     const bf16* t = cbuf<P>();
     // this wave's share of the scores, over its latent channels
     f32x16 sp = f32x16{};
@@ -323,16 +328,20 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
   load_tile(t_first, B0{});
   if (t_first + 1 < t_last) load_tile(t_first + 1, B1{});
+  if (t_first + 2 < t_last) load_tile(t_first + 2, B2{});
   int tile = t_first;
-  for (; tile + 2 < t_last; tile += 3) {
+  for (; tile + 3 < t_last; tile += 4) {
     step(tile, B0{});
     step(tile + 1, B1{});
     step(tile + 2, B2{});
+    step(tile + 3, B3{});
   }
   if (tile < t_last) step(tile, B0{});
   if (tile + 1 < t_last) step(tile + 1, B1{});
+  if (tile + 2 < t_last) step(tile + 2, B2{});
 
   // ---- partials of this split: (m, l) per head, and this wave's channels of u
   const float l_tot = swap_halves_sum(l_run);

@@ -238,7 +238,8 @@ def latent_inputs(B, N, H, dc, dev, seed, gate, packed=False):
 @pytest.mark.parametrize("B,N,H,dc,gate,splits,packed", [
     (2, 300, 4, 128, True, 0, False), (2, 1, 3, 256, False, 0, False), (1, 33, 40, 512, True, 3, False),
     (3, 1000, 8, 512, False, 7, True), (2, 64, 2, 128, False, 2, False), (1, 31, 1, 512, True, 0, False),
-    (2, 777, 33, 256, True, 1, True), (1, 4100, 5, 512, False, 0, False)])
+    (2, 777, 33, 256, True, 1, True), (1, 4100, 5, 512, False, 0, False),
+    (1, 96, 2, 512, False, 1, False), (1, 200, 3, 256, True, 1, False), (2, 190, 2, 128, False, 1, False)])
 def test_decode_latent_cache(B, N, H, dc, gate, splits, packed):
     """Decode over the latent cache (keys and values never formed) on every head, against
     the oracle's composition: ragged cache lengths (1, 31, 33 against the 32-row tiles),
@@ -256,6 +257,41 @@ def test_decode_latent_cache(B, N, H, dc, gate, splits, packed):
     got = host(out).reshape(B, H, 128)
     for (b, h), r in ref.items():
         check_rows_rel(got[b, h][None], r, 128)
+
+
+def test_decode_latent_graph_replay_matches_eager():
+    """The latent-cache decode captured in a HIP graph: replayed three times, with new
+    queries written eagerly and the stream synchronised between replays, every replay's
+    output equals an eager call on the same inputs bit for bit."""
+    dev = need_gpu()
+    announce("decode latent graph replay")
+    B, N, H, dc = 3, 1001, 40, 512
+    q, c, wk, wv, g = latent_inputs(B, N, H, dc, dev, 3950, True)
+    ws = torch.empty(gm.decode_latent_workspace_bytes(B, H, N, dc), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H * 128), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gm.attend_decode_latent(q, c, wk, wv, g, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gm.attend_decode_latent(q, c, wk, wv, g, workspace=ws, out=out)
+    for rep in range(3):
+        q.copy_(I.normal((B, H, 128), torch.bfloat16, dev, seed=3960 + rep))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = gm.attend_decode_latent(q, c, wk, wv, g)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}"
+    heads = [(0, 0), (1, 17), (2, 39)]
+    ref = oracle_latent_decode(q, c, wk, wv, g, heads)
+    hgot = host(got).reshape(B, H, 128)
+    for (b, h), r in ref.items():
+        check_rows_rel(hgot[b, h][None], r, 128)
 
 
 def test_decode_latent_matches_direct_decode_on_expanded_cache():
