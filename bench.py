@@ -401,6 +401,31 @@ def summarize_counters(d, kernel, name, cmd):
     print(out)
 
 
+def summarize_ramp(dirs, labels, name, cmd, n=60):
+    """Per-dispatch durations of the first n prefill launches of each run (a GPU starting
+    from idle), side by side, from kernel traces."""
+    cols = []
+    for d in dirs:
+        v = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                   for r in _read_csvs(d, "kernel_trace.csv") if "prefill_bf16_kernel" in r["Kernel_Name"])
+        if len(v) < n:
+            sys.exit(f"fewer than {n} prefill dispatches under {d}")
+        cols.append([x[1] / 1e3 for x in v[:n]])
+    lines = [f"# {name}", "", "Command:", "", "```", cmd, "```", "",
+             "Duration (us) of the first prefill launches after an idle GPU, in launch order.", "",
+             "| launch | " + " | ".join(labels) + " |", "|---" * (len(labels) + 1) + "|"]
+    for i in range(n):
+        lines.append(f"| {i} | " + " | ".join(f"{c[i]:.1f}" for c in cols) + " |")
+    lines += ["", "| mean of launches | " + " | ".join(labels) + " |", "|---" * (len(labels) + 1) + "|"]
+    for a, b in ((0, 10), (10, 40), (40, n)):
+        lines.append(f"| {a} .. {b - 1} | " + " | ".join(f"{sum(c[a:b]) / (b - a):.1f}" for c in cols) + " |")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def summarize_mfma(d, name, cmd):
     """MFMA utilisation of every GPU kernel in a --pmc pass with SQ_VALU_MFMA_BUSY_CYCLES
     and GRBM_GUI_ACTIVE: busy cycles summed over the 1024 SIMDs, against the dispatch's
@@ -454,6 +479,11 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=4, metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--summarize-mfma", metavar="DIR")
+    ap.add_argument("--summarize-ramp", nargs="+", metavar="DIR=LABEL",
+                    help="first prefill dispatches of each kernel-trace directory, side by side")
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="with --only prefill: all-zero Q, K and V (a diagnostic: the same work on "
+                         "data that draws little power)")
     ap.add_argument("--loop", type=float, metavar="SECONDS",
                     help="with --only prefill: call it back to back for SECONDS, printing rates")
     ap.add_argument("--name")
@@ -469,6 +499,9 @@ def main():
         return summarize_counters(args.summarize_counters, args.kernel, args.name, args.cmd)
     if args.summarize_mfma:
         return summarize_mfma(args.summarize_mfma, args.name, args.cmd)
+    if args.summarize_ramp:
+        pairs = [a.split("=", 1) for a in args.summarize_ramp]
+        return summarize_ramp([p[0] for p in pairs], [p[1] for p in pairs], args.name, args.cmd)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               f"sharding is described, not built.", file=sys.stderr)
@@ -506,6 +539,10 @@ def main():
         pw = I.WORKLOADS["prefill_b2_t4096"]
         d = pw.dims
         q, k, v, _ = I.workload_inputs(pw.name, dev)
+        if args.zero_inputs:
+            if only != "prefill":
+                sys.exit("--zero-inputs is a diagnostic for --only prefill")
+            q.zero_(), k.zero_(), v.zero_()
         out = torch.empty((d["B"], d["T"], d["H"] * d["D"]), dtype=q.dtype, device=dev)
         flops = prefill_flops(d["B"], d["T"], d["H"], d["D"])
         if args.loop:
@@ -517,7 +554,7 @@ def main():
         result.update({
             "value": round(tflops, 2), "ms_per_step": round(wall * 1e3 / K, 4),
             "config": {"workload": pw.name, "B": d["B"], "T": d["T"], "H": d["H"], "D": d["D"],
-                       "causal": True, "inputs": "N(0,1) rounded to bf16, seeded"},
+                       "causal": True, "inputs": "all zero (diagnostic)" if args.zero_inputs else "N(0,1) rounded to bf16, seeded"},
             "clock_settle": {"seconds": args.settle, "calls": settle_calls,
                              "note": "untimed back-to-back calls before the warm-up, so that the "
                                      "timed calls run at the sustained clock"},
@@ -589,6 +626,9 @@ def main():
             ld = lw.dims
             x, wts = I.workload_inputs(lw.name, dev)
             largs = (x, wts["Wq"], wts["Wc"], wts["Wk"], wts["Wv"], wts["Wg"], wts["Wo"], ld["H"], True)
+            # both forms timed at the sustained clock (otherwise the first one timed also
+            # pays for the clock's settling)
+            settle(torch, lambda i: gm.gated_mla(*largs), args.settle)
             lavg, _, _ = time_calls(torch, lambda i: gm.gated_mla(*largs), max(5, K // 5),
                                     max(2, W // 3))
             favg, _, _ = time_calls(torch, lambda i: gm.gated_mla(*largs, fused_latent=True),
