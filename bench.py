@@ -121,6 +121,46 @@ def time_calls(torch, fn, steps, warmup, rotate=1):
     return region / steps, fastest, wall
 
 
+LATENT_SWEEP = (1, 2, 4, 7, 8, 16)
+
+
+def lib_ranges(N, requested):
+    """Key ranges the latent decode uses when `requested` are asked for (rounded to whole
+    32-row tiles, none empty)."""
+    rows = -(-N // requested)
+    rows = -(-rows // 32) * 32
+    return -(-N // rows)
+
+
+def summarize_sweep(d, name, cmd):
+    """Per-kernel kernel-trace durations of the latent decode range sweep: calls are three
+    launches each, 20 untimed and 40 timed per range count, in LATENT_SWEEP order after the
+    benchmark's own calls; the averages cover the 40 timed calls."""
+    seq = sorted((int(r["Start_Timestamp"]), r["Kernel_Name"],
+                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                 for r in _read_csvs(d, "kernel_trace.csv") if "latent_" in r["Kernel_Name"])
+    per = 60 * 3
+    block = seq[len(seq) - per * len(LATENT_SWEEP):]
+    lines = [f"# {name}", "", "Command:", "", "```", cmd, "```", "",
+             "Latent-cache decode B8 H96 N1001 d_c 512 at several key-range counts; "
+             "kernel-trace averages (us) over 40 timed calls each.", "",
+             "| ranges | absorb | split | merge | sum |", "|---|---|---|---|---|"]
+    for j, sp in enumerate(LATENT_SWEEP):
+        calls = block[j * per:(j + 1) * per][20 * 3:]
+        avg = {}
+        for part in ("absorb", "split", "merge"):
+            v = [x[2] for x in calls if f"latent_{part}" in x[1]]
+            avg[part] = sum(v) / len(v) / 1e3
+        used = lib_ranges(1001, sp)
+        lines.append(f"| {used} | {avg['absorb']:.1f} | {avg['split']:.1f} | {avg['merge']:.1f} | "
+                     f"{sum(avg.values()):.1f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def settle(torch, fn, seconds):
     """Call fn back to back for about `seconds`, untimed.  From idle, a GPU's first few
     dozen calls of sustained matrix-core work run up to 30% slower than the rest while its
@@ -300,7 +340,16 @@ def _short(name: str) -> str:
     return name if len(name) < 90 else name[:87] + "..."
 
 
-def summarize_stats(d, name, cmd, window=None):
+def _bench_line(log):
+    """The benchmark's JSON line from the log of the profiled run."""
+    with open(log) as f:
+        lines = [l for l in f if l.startswith("{")]
+    if not lines:
+        sys.exit(f"no JSON line in {log}")
+    return lines[-1].strip()
+
+
+def summarize_stats(d, name, cmd, window=None, log=None):
     rows = _read_csvs(d, "kernel_stats.csv")
     if not rows:
         sys.exit(f"no *kernel_stats.csv under {d}")
@@ -331,6 +380,9 @@ def summarize_stats(d, name, cmd, window=None):
             warm = sum(x[1] for x in v[:w]) / max(w, 1) / 1e3
             timed = sum(x[1] for x in v[w:w + k]) / k / 1e3
             lines.append(f"| {_short(kname)} | {warm:.1f} | {timed:.1f} |")
+    if log:
+        lines += ["", "The benchmark's own line from the same run (event timing; under the "
+                      "profiler):", "", "```", _bench_line(log), "```"]
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"{name}.md")
     with open(out, "w") as f:
@@ -481,6 +533,9 @@ def main():
     ap.add_argument("--summarize-mfma", metavar="DIR")
     ap.add_argument("--summarize-ramp", nargs="+", metavar="DIR=LABEL",
                     help="first prefill dispatches of each kernel-trace directory, side by side")
+    ap.add_argument("--latent-sweep", action="store_true",
+                    help="with --only decode_latent: also time key-range counts " + str(LATENT_SWEEP))
+    ap.add_argument("--summarize-sweep", metavar="DIR")
     ap.add_argument("--zero-inputs", action="store_true",
                     help="with --only prefill: all-zero Q, K and V (a diagnostic: the same work on "
                          "data that draws little power)")
@@ -490,15 +545,19 @@ def main():
     ap.add_argument("--kernel")
     ap.add_argument("--key", help="record name in traffic.json (default: the kernel)")
     ap.add_argument("--cmd", default="")
+    ap.add_argument("--log", help="with --summarize-stats: the profiled run's output, whose JSON "
+                                  "line is appended")
     args = ap.parse_args()
     if args.summarize_stats:
-        return summarize_stats(args.summarize_stats, args.name, args.cmd, args.timed_window)
+        return summarize_stats(args.summarize_stats, args.name, args.cmd, args.timed_window, args.log)
     if args.summarize_traffic:
         return summarize_traffic(*args.summarize_traffic, args.kernel, args.cmd, args.key)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.kernel, args.name, args.cmd)
     if args.summarize_mfma:
         return summarize_mfma(args.summarize_mfma, args.name, args.cmd)
+    if args.summarize_sweep:
+        return summarize_sweep(args.summarize_sweep, args.name, args.cmd)
     if args.summarize_ramp:
         pairs = [a.split("=", 1) for a in args.summarize_ramp]
         return summarize_ramp([p[0] for p in pairs], [p[1] for p in pairs], args.name, args.cmd)
@@ -713,6 +772,28 @@ def main():
                 "rotation": "8 input sets (270 MB) cycled",
                 "note": "latent cache + W_k + W_v read per call (keys and values never formed): "
                         "absorb, split attention over the latent rows, merge + W_v"}
+            if args.latent_sweep:
+                # the same call at several key-range counts: 20 untimed and 40 timed calls
+                # each, in this order (the kernel trace of such a run is grouped by
+                # --summarize-sweep)
+                sweep = []
+                for sp in LATENT_SWEEP:
+                    sws = torch.empty(gm.decode_latent_workspace_bytes(B_, H_, N_, dc, sp),
+                                      dtype=torch.uint8, device=dev)
+
+                    def dec_sp(i, sp=sp, sws=sws):
+                        ql, cl, wkl, wvl, ol = lsets[i]
+                        gm.attend_decode_latent(ql, cl, wkl, wvl, workspace=sws, out=ol,
+                                                num_splits=sp)
+
+                    for i in range(20):
+                        dec_sp(i % 8)
+                    torch.cuda.synchronize()
+                    savg, _, _ = time_calls(torch, dec_sp, 40, 0, rotate=8)
+                    used = lib_ranges(N_, sp)
+                    sweep.append({"ranges_requested": sp, "ranges": used,
+                                  "avg_call_ms": round(savg, 5)})
+                extra["decode_latent_range_sweep"] = sweep
             del lsets, lws, graph
         result["extra"] = extra
 
