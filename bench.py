@@ -122,6 +122,7 @@ def time_calls(torch, fn, steps, warmup, rotate=1):
 
 
 LATENT_SWEEP = (1, 2, 4, 7, 8, 16)
+SWEEP_UNTIMED, SWEEP_TIMED, SWEEP_AFTER = 20, 40, 50  # time_calls adds five 10-call runs
 
 
 def lib_ranges(N, requested):
@@ -134,19 +135,20 @@ def lib_ranges(N, requested):
 
 def summarize_sweep(d, name, cmd):
     """Per-kernel kernel-trace durations of the latent decode range sweep: calls are three
-    launches each, 20 untimed and 40 timed per range count, in LATENT_SWEEP order after the
-    benchmark's own calls; the averages cover the 40 timed calls."""
+    launches each; per range count (in LATENT_SWEEP order, after the benchmark's own calls)
+    SWEEP_UNTIMED warm-up calls, SWEEP_TIMED timed ones and SWEEP_AFTER more; the averages
+    cover the timed calls."""
     seq = sorted((int(r["Start_Timestamp"]), r["Kernel_Name"],
                   int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
                  for r in _read_csvs(d, "kernel_trace.csv") if "latent_" in r["Kernel_Name"])
-    per = 60 * 3
+    per = (SWEEP_UNTIMED + SWEEP_TIMED + SWEEP_AFTER) * 3
     block = seq[len(seq) - per * len(LATENT_SWEEP):]
     lines = [f"# {name}", "", "Command:", "", "```", cmd, "```", "",
              "Latent-cache decode B8 H96 N1001 d_c 512 at several key-range counts; "
-             "kernel-trace averages (us) over 40 timed calls each.", "",
+             f"kernel-trace averages (us) over {SWEEP_TIMED} timed calls each.", "",
              "| ranges | absorb | split | merge | sum |", "|---|---|---|---|---|"]
     for j, sp in enumerate(LATENT_SWEEP):
-        calls = block[j * per:(j + 1) * per][20 * 3:]
+        calls = block[j * per:(j + 1) * per][SWEEP_UNTIMED * 3:(SWEEP_UNTIMED + SWEEP_TIMED) * 3]
         avg = {}
         for part in ("absorb", "split", "merge"):
             v = [x[2] for x in calls if f"latent_{part}" in x[1]]
@@ -786,10 +788,7 @@ def main():
                         gm.attend_decode_latent(ql, cl, wkl, wvl, workspace=sws, out=ol,
                                                 num_splits=sp)
 
-                    for i in range(20):
-                        dec_sp(i % 8)
-                    torch.cuda.synchronize()
-                    savg, _, _ = time_calls(torch, dec_sp, 40, 0, rotate=8)
+                    savg, _, _ = time_calls(torch, dec_sp, SWEEP_TIMED, SWEEP_UNTIMED, rotate=8)
                     used = lib_ranges(N_, sp)
                     sweep.append({"ranges_requested": sp, "ranges": used,
                                   "avg_call_ms": round(savg, 5)})
