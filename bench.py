@@ -697,6 +697,7 @@ def main():
             T_, dm, dc = ld["T"], ld["d_model"], ld["d_c"]
             lflops = 2 * T_ * (3 * dm * dm + 3 * dm * dc) + prefill_flops(1, T_, ld["H"], dm // ld["H"])
             extra[lw.name] = {"value": round(lflops / (lavg * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+                              "frac": round(lflops / (lavg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "avg_call_ms": round(lavg, 4), "algorithmic_flop": lflops,
                               "fused_latent": {"value": round(lflops / (favg * 1e-3) / 1e12, 1),
                                                "avg_call_ms": round(favg, 4),
@@ -711,6 +712,7 @@ def main():
                                     max(2, W // 10))
             cb = decode_bytes(cd["B"], cd["H"], cd["N"], cd["D"])
             extra[cw.name] = {"value": round(cb / (cavg * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "frac": round(cb / (cavg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                               "avg_call_ms": round(cavg, 4), "algorithmic_bytes": cb,
                               "splits": gm.decode_num_splits(cd["B"], cd["H"], cd["N"], cd["D"])}
             del qc, kc, vc
