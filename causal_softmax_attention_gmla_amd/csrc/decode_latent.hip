@@ -177,7 +177,8 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
   const int head = hb * HB + l32;
   const bool hvalid = head < a.H;
   const int n0 = split * a.kps;
-  const int n1 = min(a.N, n0 + a.kps);
+  // (the ranges' ends, rounded up to whole tiles, can pass 2^31 for N near the key limit)
+  const int n1 = (int)min((int64_t)a.N, (int64_t)n0 + a.kps);
   const int wd0 = wave * WDC;
   const bf16* Cb = a.c + (int64_t)b * a.csb;
   const int64_t csn = a.csn;
