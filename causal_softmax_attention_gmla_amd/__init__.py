@@ -370,7 +370,7 @@ def attend_decode_latent(q: torch.Tensor, latent_cache: torch.Tensor, key_up_pro
                          value_up_projection: torch.Tensor, gate: torch.Tensor | None = None, *,
                          scale: float | None = None, num_splits: int = 0,
                          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                         stream=None) -> torch.Tensor:
+                         kv_lens: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Decode over the latent cache: the cache holds only C [B, N, d_c]; the keys and values
     K_h = C W_k,h^T, V_h = C W_v,h^T are never formed ("Gated MLA", "Start from familiar
     attention" and "Common mistakes to avoid"; "Le Transformer et l'attention", "MLA —
@@ -380,7 +380,9 @@ def attend_decode_latent(q: torch.Tensor, latent_cache: torch.Tensor, key_up_pro
 
     q: [B, H, D] contiguous; latent_cache: [B, N, d_c] with a contiguous last axis (row
     strides free); key/value up-projections [H*D, d_c] contiguous; gate: optional
-    [B, H*D].  Returns [B, H*D].
+    [B, H*D].  kv_lens (optional int32 device tensor [B]): row b holds only its first
+    kv_lens[b] latent rows (clamped to [0, N]; its query sits at position kv_lens[b] - 1;
+    an empty row gives zeros).  Returns [B, H*D].
     """
     if q.dim() != 3 or latent_cache.dim() != 3:
         raise ValueError("q must be [B, H, D] and latent_cache [B, N, d_c]")
@@ -411,6 +413,17 @@ def attend_decode_latent(q: torch.Tensor, latent_cache: torch.Tensor, key_up_pro
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     strides = (ctypes.c_int64 * 2)(latent_cache.stride(0), latent_cache.stride(1))
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or kv_lens.shape != (B,) or not kv_lens.is_contiguous():
+            raise ValueError("kv_lens must be a contiguous int32 tensor [B]")
+        _dev(q, kv_lens)
+        st = lib.gmla_attend_decode_latent_varlen(_dtype(q), B, H, N, D, d_c, float(scale), _ptr(q),
+                                                  _ptr(latent_cache), strides, _ptr(kv_lens),
+                                                  _ptr(key_up_projection), _ptr(value_up_projection),
+                                                  _ptr(gate), _ptr(out), _ptr(workspace), ws_bytes,
+                                                  int(num_splits), _stream(dev, stream))
+        _lib.check(st, "gmla_attend_decode_latent_varlen")
+        return out
     st = lib.gmla_attend_decode_latent(_dtype(q), B, H, N, D, d_c, float(scale), _ptr(q),
                                        _ptr(latent_cache), strides, _ptr(key_up_projection),
                                        _ptr(value_up_projection), _ptr(gate), _ptr(out),

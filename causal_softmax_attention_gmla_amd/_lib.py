@@ -44,6 +44,8 @@ SIGNATURES = {
     "gmla_decode_latent_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "gmla_attend_decode_latent": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i64p, _vp, _vp, _vp,
                                        _vp, _vp, ctypes.c_size_t, _i, _vp]),
+    "gmla_attend_decode_latent_varlen": (_i, [_i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i64p, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, ctypes.c_size_t, _i, _vp]),
     "gmla_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "gmla_attend_decode_noalloc": (_i, [_i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _i64p, _vp, _vp, _i,
                                         _vp]),

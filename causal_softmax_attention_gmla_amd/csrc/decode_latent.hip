@@ -176,9 +176,12 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int head = hb * HB + l32;
   const bool hvalid = head < a.H;
+  // rows cached for this batch row: all N, or its own length (a range past it is empty
+  // and leaves m = -inf, l = 0, which the merge weighs 0)
+  const int Nb = a.lens ? min(max(a.lens[b], 0), a.N) : a.N;
   const int n0 = split * a.kps;
   // (the ranges' ends, rounded up to whole tiles, can pass 2^31 for N near the key limit)
-  const int n1 = (int)min((int64_t)a.N, (int64_t)n0 + a.kps);
+  const int n1 = (int)min((int64_t)Nb, (int64_t)n0 + a.kps);
   const int wd0 = wave * WDC;
   const bf16* Cb = a.c + (int64_t)b * a.csb;
   const int64_t csn = a.csn;
@@ -204,7 +207,7 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
   }
   auto load_tile = [&](int tile, auto buf) __attribute__((always_inline)) {
     const int r0 = tile * KT;
-    const int rows = min(KT, a.N - r0);
+    const int rows = min(KT, Nb - r0);
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(Cb + (int64_t)r0 * csn), (short)0, (int)((int64_t)(rows - 1) * csn * 2 + DC * 2),
         kBufferDword3);
@@ -286,11 +289,11 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
       s[4 * q4] = v[0]; s[4 * q4 + 1] = v[1]; s[4 * q4 + 2] = v[2]; s[4 * q4 + 3] = v[3];
     }
     // rows past the cache end score -inf (zeros were loaded there)
-    if (tile * KT + KT > a.N) {
+    if (tile * KT + KT > Nb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = tile * KT + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key >= a.N) s[r] = -INFINITY;
+        if (key >= Nb) s[r] = -INFINITY;
       }
     }
     float mt = s[0];
@@ -330,7 +333,7 @@ __device__ __forceinline__ void latent_split_body(const LatentDecodeArgs& a) {
   using B1 = std::integral_constant<int, 1>;
   using B2 = std::integral_constant<int, 2>;
   using B3 = std::integral_constant<int, 3>;
-  load_tile(t_first, B0{});
+  if (t_first < t_last) load_tile(t_first, B0{});
   if (t_first + 1 < t_last) load_tile(t_first + 1, B1{});
   if (t_first + 2 < t_last) load_tile(t_first + 2, B2{});
   int tile = t_first;
@@ -417,7 +420,9 @@ __global__ __launch_bounds__(NT) void latent_merge_kernel(LatentDecodeArgs a) {
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-    if (lane == 0) inv_l[wave] = 1.0f / l;
+    // (a row with no cached token, possible only with per-row lengths, has l = 0 and
+    // gets zeros)
+    if (lane == 0) inv_l[wave] = l > 0.0f ? 1.0f / l : 0.0f;
   }
   __syncthreads();
   // merged, normalised u of every row; thread t takes channels t + NT e.  Rows past the

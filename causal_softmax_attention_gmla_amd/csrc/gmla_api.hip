@@ -404,11 +404,14 @@ size_t gmla_decode_latent_workspace_bytes(int B, int H, int N, int d_c, int num_
   return latent_ws_bytes(B, H, d_c, splits);
 }
 
-int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, float scale,
-                              const void* Q, const void* C, const int64_t* c_strides,
-                              const void* W_k, const void* W_v, const void* G, void* O,
-                              void* workspace, size_t workspace_bytes, int num_splits,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_latent_impl(int dtype, int B, int H, int N, int D, int d_c, float scale,
+                       const void* Q, const void* C, const int64_t* c_strides, const int* lens,
+                       const void* W_k, const void* W_v, const void* G, void* O,
+                       void* workspace, size_t workspace_bytes, int num_splits, void* stream) {
   if (!valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 || D <= 0 || d_c <= 0)
     return GMLA_ERR_INVALID_ARG;
   if (!Q || !C || !W_k || !W_v || !O) return GMLA_ERR_INVALID_ARG;
@@ -448,10 +451,34 @@ int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, fl
   a.g = (const bf16*)G;
   a.o = (bf16*)O;
   a.c2 = scale * kLog2e;
+  a.lens = lens;
   if (log_enabled())
-    fprintf(stderr, "gmla: decode latent B=%d H=%d N=%d d_c=%d splits=%d (%d rows each)\n", B, H,
-            N, d_c, a.splits, a.kps);
+    fprintf(stderr, "gmla: decode latent B=%d H=%d N=%d d_c=%d splits=%d (%d rows each)%s\n", B,
+            H, N, d_c, a.splits, a.kps, lens ? " per-row lengths" : "");
   return hip_status(launch_decode_latent(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, float scale,
+                              const void* Q, const void* C, const int64_t* c_strides,
+                              const void* W_k, const void* W_v, const void* G, void* O,
+                              void* workspace, size_t workspace_bytes, int num_splits,
+                              void* stream) {
+  return decode_latent_impl(dtype, B, H, N, D, d_c, scale, Q, C, c_strides, nullptr, W_k, W_v, G,
+                            O, workspace, workspace_bytes, num_splits, stream);
+}
+
+int gmla_attend_decode_latent_varlen(int dtype, int B, int H, int N, int D, int d_c, float scale,
+                                     const void* Q, const void* C, const int64_t* c_strides,
+                                     const int* kv_lens, const void* W_k, const void* W_v,
+                                     const void* G, void* O, void* workspace,
+                                     size_t workspace_bytes, int num_splits, void* stream) {
+  if (!kv_lens || !aligned(kv_lens, 4)) return GMLA_ERR_INVALID_ARG;
+  return decode_latent_impl(dtype, B, H, N, D, d_c, scale, Q, C, c_strides, kv_lens, W_k, W_v, G,
+                            O, workspace, workspace_bytes, num_splits, stream);
 }
 
 }  // extern "C"

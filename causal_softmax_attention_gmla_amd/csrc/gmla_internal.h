@@ -133,6 +133,7 @@ struct LatentDecodeArgs {
   bf16* qp;               // workspace: absorbed queries [B, H, DC]
   float* ml;              // workspace: (m, l) per (b, h, split)
   float* u;               // workspace: [B, H, splits, DC] latent sums
+  const int* lens = nullptr;  // nullable device [B]: cached rows of each batch row (<= N)
 };
 hipError_t launch_decode_latent(const LatentDecodeArgs& a, hipStream_t s);
 

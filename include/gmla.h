@@ -241,6 +241,21 @@ int gmla_attend_decode_latent(int dtype, int B, int H, int N, int D, int d_c, fl
                               void* stream);
 
 /*
+ * gmla_attend_decode_latent with a cache length per batch row: row b holds kv_lens[b]
+ * latent rows (a DEVICE array of B int32, 4-byte aligned; values are clamped to [0, N],
+ * N being the capacity that c_strides describe), and its query sits at position
+ * kv_lens[b] - 1, seeing all of them ("Kimi K2 - Construct causal mask": positions
+ * continue from the cached length).  A row with no cached token gets an all-zero output.
+ * Workspace, key ranges (planned over the capacity N), types and limits as for
+ * gmla_attend_decode_latent; kv_lens NULL is GMLA_ERR_INVALID_ARG.
+ */
+int gmla_attend_decode_latent_varlen(int dtype, int B, int H, int N, int D, int d_c, float scale,
+                                     const void* Q, const void* C, const int64_t* c_strides,
+                                     const int* kv_lens, const void* W_k, const void* W_v,
+                                     const void* G, void* O, void* workspace,
+                                     size_t workspace_bytes, int num_splits, void* stream);
+
+/*
  * gmla_attend_decode without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, serving loops and harnesses that forbid
  * allocation).  Same arguments, results and limits as gmla_attend_decode, minus the

@@ -92,6 +92,8 @@ int main(void) {
     EXPECT(gmla_attend_decode_latent(GMLA_BF16, 2, 4, 100, 128, 512, 0.1f, F, F, 0, F, F, 0, F, F, need - 1, 0, 0), GMLA_ERR_WORKSPACE);
     EXPECT(gmla_attend_decode_latent(GMLA_BF16, 2, 4, 100, 128, 512, 0.1f, F, F, 0, F, F, F, F, F, need, 0, 0), GMLA_ERR_HIP);
     EXPECT(gmla_attend_decode_latent(GMLA_BF16, 1, 40, 33, 128, 128, 0.1f, F, F, 0, F, F, 0, F, F, 1 << 20, 3, 0), GMLA_ERR_HIP);
+    EXPECT(gmla_attend_decode_latent_varlen(GMLA_BF16, 2, 4, 100, 128, 512, 0.1f, F, F, 0, 0, F, F, 0, F, F, need, 0, 0), GMLA_ERR_INVALID_ARG);
+    EXPECT(gmla_attend_decode_latent_varlen(GMLA_BF16, 2, 4, 100, 128, 512, 0.1f, F, F, 0, (const int*)F, F, F, 0, F, F, need, 0, 0), GMLA_ERR_HIP);
     if (gmla_decode_latent_num_splits(8, 96, 1001, 512) != 7) ++failures;
   }
   /* projections */
@@ -107,6 +109,8 @@ int main(void) {
   EXPECT(gmla_gate_out(GMLA_BF16, 4, 16, 0, 0, 0, F, 0), GMLA_ERR_INVALID_ARG);
   EXPECT(gmla_gate_out(GMLA_BF16, 64, 128, F, F, F, F, 0), GMLA_ERR_HIP);
   EXPECT(gmla_gate_out(GMLA_BF16, 64, 128, F, F, 0, F, 0), GMLA_ERR_HIP);
+  EXPECT((int)gmla_gate_out_workspace_bytes(GMLA_BF16, 64, 128), 64 * 128 * 2);
+  EXPECT(gmla_gate_out_ws(GMLA_BF16, 64, 128, F, F, F, F, (void*)((char*)F + (1 << 24)), 64 * 128 * 2, 0), GMLA_ERR_HIP);
   if (gmla_status_string(GMLA_ERR_HIP)[0] != 'G') ++failures;
   printf("host sanitized run: %d failures\n", failures);
   return failures != 0;

@@ -232,6 +232,24 @@ def test_decode_latent_limits_and_workspace():
         r256(768 * 512 * 2) + r256(768 * s * 8) + 768 * s * 512 * 4
 
 
+def _latent_varlen(**kw):
+    a = dict(dtype=1, B=2, H=4, N=100, D=128, d_c=512, scale=0.1, Q=FAKE, C=FAKE, c_strides=None,
+             lens=FAKE, W_k=FAKE, W_v=FAKE, G=None, O=FAKE, ws=FAKE, ws_bytes=1 << 30, splits=0,
+             stream=None)
+    a.update(kw)
+    return gm.library().gmla_attend_decode_latent_varlen(*a.values())
+
+
+def test_decode_latent_varlen_arguments():
+    assert _latent_varlen(lens=None) == -1
+    assert _latent_varlen(lens=ctypes.c_void_p((1 << 20) + 2)) == -1  # not 4-byte aligned
+    assert _latent_varlen(N=0) == -1
+    assert _latent_varlen(C=None) == -1
+    assert _latent_varlen(d_c=384) == -2
+    assert _latent_varlen(N=MAX_KEYS + 1) == -2
+    assert _latent_varlen(ws=None) == -3
+
+
 def _noalloc(**kw):
     a = dict(dtype=1, B=2, H=4, N=100, D=128, scale=0.1, Q=FAKE, K=FAKE, V=FAKE, kv_strides=None,
              G=None, O=FAKE, splits=1, stream=None)
@@ -391,6 +409,7 @@ def valid_calls_without_a_device():
     assert _noalloc() == -4
     assert _noalloc(splits=4) == -4  # the scratch lookup fails without a device
     assert _latent() == -4
+    assert _latent_varlen() == -4
     assert _platent() == -4
     assert lib.gmla_linear_ws(1, 2048, 512, 12288, FAKE, FAKE, FAKE, FAKE, 1 << 26, None) == -4
     assert lib.gmla_linear_ws(1, 64, 64, 64, FAKE, FAKE, FAKE, None, 0, None) == -4

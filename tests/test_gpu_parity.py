@@ -259,6 +259,40 @@ def test_decode_latent_cache(B, N, H, dc, gate, splits, packed):
         check_rows_rel(got[b, h][None], r, 128)
 
 
+@pytest.mark.parametrize("dc,splits,gate", [(512, 0, True), (512, 7, False), (128, 3, True)])
+def test_decode_latent_per_row_lengths(dc, splits, gate):
+    """Latent-cache decode with a cache length per batch row (0, 1, 31, 33, 700 and the
+    full capacity): each row against the oracle's composition over its own rows (an empty
+    row is zeros), key ranges past a row's length left empty, and a full-length row equal
+    to the fixed-length call bit for bit."""
+    dev = need_gpu()
+    announce(f"decode over latent cache, per-row lengths, d_c={dc} splits={splits}")
+    lens = [0, 1, 31, 33, 700, 1000]
+    B, N, H = len(lens), 1000, 5
+    q, c, wk, wv, g = latent_inputs(B, N, H, dc, dev, 3970 + dc + splits, gate)
+    kv = torch.tensor(lens, dtype=torch.int32, device=dev)
+    out = torch.full((B, H * 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.attend_decode_latent(q, c, wk, wv, g, num_splits=splits, out=out, kv_lens=kv)
+    full = gm.attend_decode_latent(q, c, wk, wv, g, num_splits=splits)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    got = host(out).reshape(B, H, 128)
+    assert np.all(got[0] == 0.0)
+    assert torch.equal(out[B - 1], full[B - 1])
+    hq, hc, hwk, hwv = host(q), host(c), host(wk), host(wv)
+    hg = host(g) if g is not None else None
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        for h in range(H):
+            kh = oracle.linear(hc[b, :n], hwk[h * 128:(h + 1) * 128])
+            vh = oracle.linear(hc[b, :n], hwv[h * 128:(h + 1) * 128])
+            ref = oracle.attend_head(hq[b, h][None, :], kh, vh, 1 / np.sqrt(128), True)
+            if hg is not None:
+                ref = oracle.gate(hg[b, h * 128:(h + 1) * 128][None, :], ref)
+            check_rows_rel(got[b, h][None], ref, 128)
+
+
 def test_decode_latent_graph_replay_matches_eager():
     """The latent-cache decode captured in a HIP graph: replayed three times, with new
     queries written eagerly and the stream synchronised between replays, every replay's
