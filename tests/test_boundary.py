@@ -439,3 +439,41 @@ def test_valid_call_without_a_device_returns_hip_error():
         pytest.skip("a HIP device is visible")
     assert r.returncode == 0, r.stdout + r.stderr[-3000:]
     assert "no-device calls ok" in r.stdout
+
+
+def _bench_module():
+    import importlib.util
+    here = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(here, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_bench_range_labels_match_the_library_plan():
+    """The latent range sweep labels each run with the range count the library uses for a
+    requested count; that count is read back here from the workspace size the library
+    asks for (absorbed queries, then (m, l) and d_c sums per range)."""
+    bench = _bench_module()
+    lib = gm.library()
+    B, H, dc = 8, 96, 512
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for N in (1, 31, 33, 1001, 4100, 131072):
+        for req in (1, 2, 3, 4, 7, 8, 10, 16, 1000):
+            ws = lib.gmla_decode_latent_workspace_bytes(B, H, N, dc, req)
+            used = bench.lib_ranges(N, req)
+            assert ws == r256(B * H * dc * 2) + r256(B * H * used * 8) + B * H * used * dc * 4, (N, req)
+
+
+def test_bench_source_digest_ignores_comments_only(tmp_path):
+    """Recorded counters stay valid across comment edits and are voided by code edits."""
+    bench = _bench_module()
+    src = tmp_path / "k.hip"
+    bench.HERE = str(tmp_path)
+    bench.KERNEL_SOURCES = {"k": ["k.hip"]}
+    src.write_text("int a = 1;  // one\n\n// note\nint b = 2;\n")
+    d0 = bench.source_digest("k")
+    src.write_text("int a = 1;  // changed comment\n// another note\n\nint b = 2;\n")
+    assert bench.source_digest("k") == d0
+    src.write_text("int a = 1;\nint b = 3;\n")
+    assert bench.source_digest("k") != d0
