@@ -297,7 +297,7 @@ int gmla_gate_out(int dtype, int M, int d_model, const void* G, const void* O_ti
  * gmla_gate_out with a caller workspace, for bf16 with both a gate and W_o: the gate is
  * applied by its own pass into the workspace (sigmoid(G) (.) O~ rounded to bf16, the same
  * operand gmla_gate_out forms while staging its GEMM tiles) and the projection then runs
- * on the LDS-pipelined GEMM.  At M = 2048, d_model = 12288 that is about 0.54 ms instead
+ * on the LDS-pipelined GEMM.  At M = 2048, d_model = 12288 that is about 0.5 ms instead
  * of 2.0 ms.  gmla_gate_out_workspace_bytes(dtype, M, d_model) is the space it needs
  * (M * d_model * 2 bytes; 0 for fp32 and for d_model not a multiple of 64).  With no
  * gate, no W_o, fp32, or a NULL, misaligned (16 bytes) or smaller workspace the call is
