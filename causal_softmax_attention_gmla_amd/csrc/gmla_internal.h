@@ -44,9 +44,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Logistic sigmoid in f32: 1 / (1 + e^-x), with e^-x = 2^(-x log2 e).
+// Logistic sigmoid in f32: 1 / (1 + e^-x), with e^-x = 2^(-x log2 e) and the hardware
+// reciprocal (1 ulp) in place of an IEEE division; x -> -inf gives 1/inf = 0, x -> +inf
+// gives 1/1 = 1.
 __device__ __forceinline__ float sigmoidf_(float x) {
-  return 1.0f / (1.0f + __expf(-x));
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
 }
 
 // Element loads/stores generic over float and bf16 storage.

@@ -336,6 +336,28 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
   // bits 4..7).
   const int kfrag = l32 * 256 + ((hh ^ (l32 & 15)) << 4);
 
+  // Output staging: each wave's 32 rows x 128 channels (bf16, 8 KB) in its own quarter of
+  // the two K buffers, which no wave reads after the second-to-last tile.  With a gate,
+  // the gate logits of those rows arrive there first: requested (whole 256-byte rows,
+  // LDS-direct) when the last tile starts, so the epilogue finds them in LDS instead of
+  // waiting for scattered 8-byte global reads.  Row r's 16-byte unit u sits at unit
+  // u ^ (r mod 16) in both.
+  char* const ep = (char*)(wave < 2 ? lds_k0 : lds_k1) + (wave & 1) * 8192;
+  const int64_t hd = (int64_t)a.H * HD;
+  const int grows = min(32, T - wq0);  // rows of this wave inside the sequence
+  const bool gate_lds = a.g && grows > 0 && 31 * hd + HD < ((int64_t)1 << 30);
+  auto load_gate = [&]() __attribute__((always_inline)) {
+    const bf16* gbase = (const bf16*)a.g + (qrow0 + wq0) * hd + (int64_t)h * HD;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)gbase, (short)0, (int)(((int64_t)(grows - 1) * hd + HD) * 2), kBufferDword3);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = 4 * u + (lane >> 4);
+      load_lds16(r, (bf16*)(ep + u * 1024),
+                 (uint32_t)((row * hd + (((lane & 15) ^ (row & 15)) << 3)) * 2));
+    }
+  };
+
   // One iteration: weights of tile j, values of tile j, scores of tile j+1, as a fixed
   // interleave of 32 MFMA groups (the fences keep the order): each group issues one
   // MFMA, requests the LDS fragments of the MFMA two groups on, and carries a share of
@@ -415,6 +437,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
     };
 
     if constexpr (NEXT == 2) {
+      if (gate_lds) load_gate();
       // last tile: weights, then values.  A 32-key half past every key this wave's
       // queries may see holds only masked scores (weight exactly 0): its exponentials and
       // value MFMAs would add zeros, so the wave skips them.
@@ -504,28 +527,27 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
 
   // ---- epilogue: normalise, gate, round, store [B, T, H*128].  O^T leaves a lane four
   // consecutive channels of one query per register quad; stored directly, each store
-  // instruction would touch 32 query rows.  Instead each wave puts its 32 rows x 128
-  // channels (bf16, 8 KB) in its own quarter of the two K buffers, which no wave reads
-  // after the second-to-last tile, and stores whole 256-byte rows from there.  Row r's
-  // 16-byte unit u sits at unit u ^ (r mod 16), so neither side meets bank conflicts.
+  // instruction would touch 32 query rows.  Instead each wave puts its rows in the
+  // staging area above and stores whole 256-byte rows from there (no bank conflicts on
+  // either side).  A lane reads its gate logits from the very bytes it then overwrites.
   const float l_tot = swap_halves_sum(l_run);
   // (a query with no visible key, possible only with per-sequence lengths, writes zeros)
   const float inv = VARLEN ? (l_tot > 0.0f ? 1.0f / l_tot : 0.0f) : 1.0f / l_tot;
-  const int64_t hd = (int64_t)a.H * HD;
-  const bf16* __restrict__ gate = a.g ? (const bf16*)a.g + (qrow0 + tq) * hd + (int64_t)h * HD
-                                      : nullptr;
-  char* const ep = (char*)(wave < 2 ? lds_k0 : lds_k1) + (wave & 1) * 8192;
+  const bf16* __restrict__ gate =
+      a.g && !gate_lds ? (const bf16*)a.g + (qrow0 + tq) * hd + (int64_t)h * HD : nullptr;
+  if (gate_lds) __builtin_amdgcn_s_waitcnt(0);  // the gate rows have landed in LDS
 #pragma unroll
   for (int dblk = 0; dblk < 4; ++dblk)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = dblk * 32 + 8 * r4 + 4 * hh;
+      char* const slot = ep + l32 * 256 + (((d >> 3) ^ (l32 & 15)) << 4) + (d & 4) * 2;
       float v0 = o_acc[dblk][4 * r4 + 0] * inv;
       float v1 = o_acc[dblk][4 * r4 + 1] * inv;
       float v2 = o_acc[dblk][4 * r4 + 2] * inv;
       float v3 = o_acc[dblk][4 * r4 + 3] * inv;
-      if (gate && tq < T) {
-        const u32x2 gw = *(const u32x2*)(gate + d);
+      if (gate_lds || (gate && tq < T)) {
+        const u32x2 gw = gate_lds ? *(const u32x2*)slot : *(const u32x2*)(gate + d);
         v0 *= sigmoidf_(bf16_lo(gw[0]));
         v1 *= sigmoidf_(bf16_hi(gw[0]));
         v2 *= sigmoidf_(bf16_lo(gw[1]));
@@ -534,7 +556,7 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
       u32x2 w;
       w[0] = pack_bf16x2(v0, v1);
       w[1] = pack_bf16x2(v2, v3);
-      *(u32x2*)(ep + l32 * 256 + (((d >> 3) ^ (l32 & 15)) << 4) + (d & 4) * 2) = w;
+      *(u32x2*)slot = w;
     }
   bf16* __restrict__ out = (bf16*)a.o + (qrow0 + wq0) * hd + (int64_t)h * HD;
 #pragma unroll
