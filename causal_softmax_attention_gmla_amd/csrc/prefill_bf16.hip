@@ -329,6 +329,9 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
   scores(B0{}, s_cur);
   if (0 >= mask_from) mask(s_cur, 0);
   float mt_cur = tile_max(s_cur);
+  // tile 0 sets the running maximum (the output and sum are still zero, so the first
+  // iteration needs no rescale)
+  m_run = mt_cur;
   __syncthreads();  // every wave has read K buffer 0 before iteration 0 refills it
 
   // K fragment of (32-key half sub, k-step ks): row 32 sub + l32, logical chunk
