@@ -177,19 +177,23 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
     for (int u = 0; u < C::WL; ++u) wo[u] = offset(8 * (wave * C::WL + u) + (lane >> 3), lane);
   }
   const int kst0 = SPLIT ? split * p.kps : 0;  // first k stage of this range
-  auto load_stage = [&](int kt, auto b) __attribute__((always_inline)) {
+  // load u of stage kt into buffer b (u < XL: rows of X, else rows of W)
+  auto load_one = [&](int kt, auto b, int u) __attribute__((always_inline)) {
     const int koff = (kst0 + kt) * BK * 2;
     const int ln = kKeepOffsets ? lane : opaque(lane);
-#pragma unroll
-    for (int u = 0; u < C::XL; ++u)
+    if (u < C::XL)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xr, (lds_void_t*)(xbuf(b) + (wave * C::XL + u) * 512), 16,
           kKeepOffsets ? xo[u] : offset(8 * (wave * C::XL + u) + (ln >> 3), ln), koff, 0, 0);
-#pragma unroll
-    for (int u = 0; u < C::WL; ++u)
+    else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr, (lds_void_t*)(wbuf(b) + (wave * C::WL + u) * 512), 16,
-          kKeepOffsets ? wo[u] : offset(8 * (wave * C::WL + u) + (ln >> 3), ln), koff, 0, 0);
+          wr, (lds_void_t*)(wbuf(b) + (wave * C::WL + (u - C::XL)) * 512), 16,
+          kKeepOffsets ? wo[u - C::XL] : offset(8 * (wave * C::WL + (u - C::XL)) + (ln >> 3), ln),
+          koff, 0, 0);
+  };
+  auto load_stage = [&](int kt, auto b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < C::LPS; ++u) load_one(kt, b, u);
   };
 
   // Fragment reads: row l32 of a 32-row group, logical chunk 2 ks + hh, at byte
@@ -204,7 +208,16 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
 
   // One stage: 4 k-steps of 16; the fragments of k-step ks+1 are requested before the
   // MFMAs of k-step ks, so their LDS latency is covered (the fences keep that order).
-  auto compute = [&](auto b) __attribute__((always_inline)) {
+  // On the 256 x 384 tiles the loads of the stage kt_next (>= 0) go out one after every
+  // second MFMA from the first on: issued in one block after the barrier, their address
+  // work (recomputed per stage on these tiles) and issue held back the first fragment
+  // reads and MFMAs of every stage (2048 x 12288 x 12288: +6-7% in alternating runs,
+  // bitwise the same result).  The other tiles keep the block: spread, the 512-deep
+  // latent expansion ran 3% slower (its next stage arrives later) and the split-K
+  // ranges the same.
+  constexpr int kMfmaPerStage = (BK / 16) * C::FM * C::FN;
+  constexpr bool kSpreadLoads = BM == 256 && BN == 384 && 2 * (C::LPS - 1) < kMfmaPerStage;
+  auto compute = [&](auto b, int kt_next, auto bn) __attribute__((always_inline)) {
     const char* xt = (const char*)xbuf(b) + wm * C::TM * 128;
     const char* wt = (const char*)wbuf(b) + wn * C::TN * 128;
     const int fl = opaque(frag_lane);
@@ -223,8 +236,17 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j)
+        for (int j = 0; j < C::FM; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][i], xf[ks & 1][j], acc[i][j], 0, 0, 0);
+          if constexpr (kSpreadLoads) {
+            const int m = (ks * C::FN + i) * C::FM + j;  // MFMA index in the stage
+            if (kt_next >= 0 && m % 2 == 0 && m / 2 < C::LPS) {
+              __builtin_amdgcn_sched_barrier(0);
+              load_one(kt_next, bn, m / 2);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -252,16 +274,19 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
     else
       wait_vmcnt<0>();
     lds_barrier();
-    if (kt + S - 1 < nk) load_stage(kt + S - 1, std::integral_constant<int, (Bc + S - 1) % S>{});
-    compute(b);
+    using Bn = std::integral_constant<int, (Bc + S - 1) % S>;
+    const int kt_next = kt + S - 1 < nk ? kt + S - 1 : -1;
+    if (!kSpreadLoads && kt_next >= 0) load_stage(kt_next, Bn{});
+    compute(b, kSpreadLoads ? kt_next : -1, Bn{});
   };
   // main loop: every step has S-2 later stages in flight and requests one more
   auto step_full = [&](int kt, auto b) __attribute__((always_inline)) {
     constexpr int Bc = decltype(b)::value;
     wait_vmcnt<(S - 2) * C::LPS>();
     lds_barrier();
-    load_stage(kt + S - 1, std::integral_constant<int, (Bc + S - 1) % S>{});
-    compute(b);
+    using Bn = std::integral_constant<int, (Bc + S - 1) % S>;
+    if (!kSpreadLoads) load_stage(kt + S - 1, Bn{});
+    compute(b, kSpreadLoads ? kt + S - 1 : -1, Bn{});
   };
   int kt = 0;
   for (; kt + 2 * S - 2 < nk; kt += S) {
