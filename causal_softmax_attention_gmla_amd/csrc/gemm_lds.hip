@@ -427,11 +427,13 @@ bool gemm_lds_supported(const GemmArgs& p) {
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& p, hipStream_t s) {
-  // Deep products (K >= 1024) with enough 256 x 384 tiles to fill the CUs: 8 waves of
+  // Deep products (K >= 512) with enough 256 x 384 tiles to fill the CUs: 8 waves of
   // 128 x 96, 2 stages (160 KB of LDS, one workgroup per CU); per flop they move 29% fewer
   // tile bytes global -> LDS and read 30% fewer fragment bytes than 256 x 192 tiles
-  // (measured on 2048 x 12288 x 12288: 1076 -> 1243 TFLOP/s), but with K = 512 their
-  // prologue weighs more (775 -> 701), so the latent expansion keeps the wide tiles.
+  // (measured on 2048 x 12288 x 12288: 1076 -> 1243 TFLOP/s).  With the tile loads issued
+  // among the MFMAs they also win at K = 512, the latent expansion (2048 x 24576 x 512:
+  // 846 -> 908 TFLOP/s in alternating runs; before that change they lost there, 775 ->
+  // 701).
   // Wide outputs: 256 x 192 tiles, 8 waves of 64 x 96, 2 stages (112 KB of LDS, one
   // workgroup per CU); measured against 256 x 128 tiles with 3 stages: 5% faster on the
   // 12288-deep projections, 16% on the 512-deep latent expansion.  Narrow outputs (too
@@ -439,7 +441,7 @@ hipError_t launch_gemm_lds(const GemmArgs& p, hipStream_t s) {
   // two workgroups per CU).
   const long deep = (long)((p.M + 255) / 256) *
                     ((p.N + 383) / 384 + (p.w2 ? (p.N2 + 383) / 384 : 0));
-  if (deep >= 256 && p.K >= 1024 && p.N % 384 == 0 && (!p.w2 || p.N2 % 384 == 0) &&
+  if (deep >= 256 && p.K >= 512 && p.N % 384 == 0 && (!p.w2 || p.N2 % 384 == 0) &&
       (int64_t)384 * p.K * 2 < ((int64_t)1 << 31))
     return launch_cfg<256, 384, 512>(gemm_lds_deep_kernel, p, s);
   const long big = (long)((p.M + 255) / 256) *

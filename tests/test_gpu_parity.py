@@ -450,10 +450,10 @@ def test_linear_mid_ragged(M, N, K):
                                    (2048, 12288, 1024), (3, 98304, 1024)])
 def test_linear_large_tiles_ragged(M, N, K):
     """Products with enough large tiles to fill the CUs: 256 x 192 tiles (the first two: N
-    not a multiple of 192, or K deep but N not a multiple of 384) and 256 x 384 tiles (K >=
-    1024 and N a multiple of 384; M not a multiple of 256, an odd number of 64-deep
-    stages, and three rows in 256-row tiles).  The output starts as NaN: every element is
-    written; sampled rows match the oracle across the full width."""
+    not a multiple of 192 with K below 512, or K deep but N not a multiple of 384) and
+    256 x 384 tiles (K >= 512 and N a multiple of 384; M not a multiple of 256, an odd
+    number of 64-deep stages, and three rows in 256-row tiles).  The output starts as NaN:
+    every element is written; sampled rows match the oracle across the full width."""
     dev = need_gpu()
     announce(f"linear large tiles {M}x{N}x{K}")
     x = I.normal((M, K), torch.bfloat16, dev, seed=4400 + K)
@@ -467,10 +467,13 @@ def test_linear_large_tiles_ragged(M, N, K):
     check_rows_rel(host(y)[rows], oracle.linear(host(x)[rows], host(w)), N)
 
 
-@pytest.mark.parametrize("M,dc,dm", [(2000, 320, 6152), (2048, 1024, 6144)])
+@pytest.mark.parametrize("M,dc,dm", [(2000, 320, 6152), (2048, 1024, 6144), (2048, 512, 6144),
+                                     (1999, 576, 6144)])
 def test_latent_expand_large_tiles(M, dc, dm):
     """Both outputs of one launch in the large-tile kernels: 256 x 192 tiles with widths
-    not a tile multiple, and 256 x 384 tiles (a 1024-wide latent); sampled rows."""
+    not a tile multiple (a 320-wide latent), and 256 x 384 tiles (latents of 1024, 512 -
+    the pages' width, eight 64-deep stages - and 576, nine stages with a ragged last
+    row block); sampled rows."""
     dev = need_gpu()
     announce(f"latent_expand large tiles {M}x{dm}x{dc}")
     c = I.normal((M, dc), torch.bfloat16, dev, seed=4120 + dc)
