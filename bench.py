@@ -382,6 +382,22 @@ def summarize_stats(d, name, cmd, window=None, log=None):
             warm = sum(x[1] for x in v[:w]) / max(w, 1) / 1e3
             timed = sum(x[1] for x in v[w:w + k]) / k / 1e3
             lines.append(f"| {_short(kname)} | {warm:.1f} | {timed:.1f} |")
+    # a library kernel that serves several shapes (one launch grid each), per grid
+    grids = {}
+    for r in _read_csvs(d, "kernel_trace.csv"):
+        if "gmla" not in r["Kernel_Name"]:
+            continue
+        wg = int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)
+        grids.setdefault(r["Kernel_Name"], {}).setdefault(wg, []).append(
+            int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    multi = {k: v for k, v in grids.items() if len(v) > 1}
+    if multi:
+        lines += ["", "Library kernels launched with more than one grid, per grid size (from the "
+                      "kernel trace):", "", "| kernel | workgroups | calls | average (us) |",
+                  "|---|---|---|---|"]
+        for kname, per in sorted(multi.items()):
+            for wg, v in sorted(per.items()):
+                lines.append(f"| {_short(kname)} | {wg} | {len(v)} | {sum(v) / len(v) / 1e3:.1f} |")
     if log:
         lines += ["", "The benchmark's own line from the same run (event timing; under the "
                       "profiler):", "", "```", _bench_line(log), "```"]
