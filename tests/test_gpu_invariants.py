@@ -142,3 +142,45 @@ def test_inputs_not_mutated():
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip((q, k, v, g), saved))
     assert all(torch.equal(a, b) for a, b in zip((qd, kd, vd, gd), saved_d))
+
+
+def _saturating_logits(shape, dtype, dev):
+    """Gate logits cycling over the channels through values far in both tails, where the
+    sigmoid is exactly 0 or 1 in float32, and zero (one half)."""
+    vals = torch.tensor([-float("inf"), -1e4, -200.0, -100.0, 0.0, 30.0, 100.0, 200.0, 1e4,
+                         float("inf")], dtype=torch.float32)
+    n = shape[-1]
+    row = vals[torch.arange(n) % len(vals)]
+    return row.expand(*shape).contiguous().to(dtype).to(dev), row
+
+
+def _check_saturation(gated, plain, row):
+    """Channels with logit <= -100 must come out exactly 0 (1 / (1 + e^100) is below the
+    float32 range), those with logit >= 30 exactly the ungated value (the sigmoid rounds
+    to 1), those with logit 0 half of it to the output rounding; nothing non-finite."""
+    g = gated.reshape(-1, row.numel())
+    p = plain.reshape(-1, row.numel())
+    assert np.all(np.isfinite(g))
+    lo, hi, mid = (row <= -100).numpy(), (row >= 30).numpy(), (row == 0).numpy()
+    assert np.all(g[:, lo] == 0.0)
+    assert np.array_equal(g[:, hi], p[:, hi])
+    assert np.max(np.abs(g[:, mid] - 0.5 * p[:, mid])) <= BF16_ULP * np.max(np.abs(p)) + 1e-7
+
+
+def test_gate_saturation_every_gated_path():
+    """The sigmoid gate at its extremes ('Gated MLA', 'The channel-wise output gate':
+    the gate scales each channel by a number in (0, 1)): the prefill epilogue (logits
+    staged through LDS), the decode epilogue, and the gate pass of the output projection
+    (bf16 and float32) give exact zeros, exact pass-through and a clean half."""
+    dev = need_gpu()
+    announce("invariant gate saturation")
+    q, k, v, _ = I.prefill_inputs(2, 200, 3, 128, torch.bfloat16, dev, seed=6800)
+    g, row = _saturating_logits((2, 200, 3 * 128), torch.bfloat16, dev)
+    _check_saturation(host(gm.attend_prefill(q, k, v, g)), host(gm.attend_prefill(q, k, v)), row)
+    qd, kd, vd, _ = I.decode_inputs(2, 3, 700, 128, torch.bfloat16, dev, seed=6801)
+    gd, row = _saturating_logits((2, 3 * 128), torch.bfloat16, dev)
+    _check_saturation(host(gm.attend_decode(qd, kd, vd, gd)), host(gm.attend_decode(qd, kd, vd)), row)
+    for dtype in (torch.bfloat16, torch.float32):
+        o = I.normal((64, 640), dtype, dev, seed=6802)
+        go, row = _saturating_logits((64, 640), dtype, dev)
+        _check_saturation(host(gm.gate_out(o, None, go)), host(o), row)
