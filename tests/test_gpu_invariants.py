@@ -129,6 +129,44 @@ def test_repeated_runs_bitwise_identical():
         assert torch.equal(gm.attend_decode(qd, kd, vd), d)
 
 
+def test_repeated_runs_bitwise_identical_projections_and_latent_forms():
+    """Run-to-run bitwise repeatability of the other kernels (a race on LDS stages, a
+    counter or a split-K partial would show as differing bits): the 256 x 384-tile GEMM
+    (loads issued among its MFMAs) and its dual-output latent expansion, the split-K
+    down-projection with its reduce, the gated output projection through the gate pass,
+    the decode over the latent cache and the latent-fused prefill."""
+    dev = need_gpu()
+    announce("invariant determinism: projections and latent forms")
+    x = I.normal((2048, 1024), torch.bfloat16, dev, seed=6900)
+    w = I.normal((12288, 1024), torch.bfloat16, dev, seed=6901, std=1024 ** -0.5)
+    c = I.normal((2048, 512), torch.bfloat16, dev, seed=6902)
+    wk = I.normal((6144, 512), torch.bfloat16, dev, seed=6903, std=512 ** -0.5)
+    wv = I.normal((6144, 512), torch.bfloat16, dev, seed=6904, std=512 ** -0.5)
+    xc = I.normal((2048, 6144), torch.bfloat16, dev, seed=6905)
+    wc = I.normal((512, 6144), torch.bfloat16, dev, seed=6906, std=6144 ** -0.5)
+    g = I.normal((2048, 6144), torch.bfloat16, dev, seed=6907)
+    wo = I.normal((6144, 6144), torch.bfloat16, dev, seed=6908, std=6144 ** -0.5)
+    q, lc, lwk, lwv, lg = (I.normal((4, 16, 128), torch.bfloat16, dev, seed=6909),
+                           I.normal((4, 1001, 512), torch.bfloat16, dev, seed=6910),
+                           I.normal((16 * 128, 512), torch.bfloat16, dev, seed=6911, std=512 ** -0.5),
+                           I.normal((16 * 128, 512), torch.bfloat16, dev, seed=6912, std=512 ** -0.5),
+                           I.normal((4, 16 * 128), torch.bfloat16, dev, seed=6913))
+    qp = I.normal((1, 640, 8, 128), torch.bfloat16, dev, seed=6914)
+    cp = I.normal((1, 640, 512), torch.bfloat16, dev, seed=6915)
+    runs = {
+        "linear 256x384 tiles": lambda: gm.linear(x, w),
+        "latent expansion": lambda: torch.cat(gm.latent_expand(c, wk, wv), dim=1),
+        "split-K down-projection": lambda: gm.linear(xc, wc),
+        "gated output projection": lambda: gm.gate_out(xc, wo, g),
+        "latent-cache decode": lambda: gm.attend_decode_latent(q, lc, lwk, lwv, lg),
+        "latent-fused prefill": lambda: gm.attend_prefill_latent(qp, cp, lwk[:1024], lwv[:1024]),
+    }
+    for name, fn in runs.items():
+        first = fn().clone()
+        for _ in range(2):
+            assert torch.equal(fn(), first), name
+
+
 def test_inputs_not_mutated():
     """'Gated MLA', 'Requirements': no input tensor is modified."""
     dev = need_gpu()
