@@ -130,9 +130,13 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
   const int bid = blockIdx.x;
   const int per_xcd = total / kNumXcd;
   const int L = bid < per_xcd * kNumXcd ? (bid % kNumXcd) * per_xcd + bid / kNumXcd : bid;
-  // split-K: the ranges of one tile are neighbours in L (the same XCD)
-  const int split = SPLIT ? L % p.splits : 0;
-  const int tile = SPLIT ? L / p.splits : L;
+  // split-K: L runs over the tiles of one range, then the next range, so an XCD takes
+  // whole ranges (with eight ranges, one each) and reads its slab of X and W from the
+  // last-level cache or HBM once for all its tiles, instead of every XCD reading
+  // slabs of every range (2048 x 512 x 12288, 8 ranges: 571 -> 695 TFLOP/s with the
+  // reduce, in alternating runs; the partials and their sum are bitwise the same)
+  const int split = SPLIT ? L / (total / p.splits) : 0;
+  const int tile = SPLIT ? L % (total / p.splits) : L;
   const int mb = tile % nmb;
   int nblk = tile / nmb;
   const bf16* W = (const bf16*)p.w;
