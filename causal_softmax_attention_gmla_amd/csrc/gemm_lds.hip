@@ -167,8 +167,13 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
   // Load u of a wave fills 8 LDS rows (1 KB) in physical chunk order: lane i writes
   // row 8 (wave * L + u) + i / 8, physical chunk i mod 8, i.e. logical chunk
   // (i mod 8) ^ ((row >> 1) & 7) of that row; the stage's k offset is the scalar part.
-  // The 256 x 384 tile keeps no offsets in registers (its accumulators take 192 of the
-  // wave's 256): they are recomputed at each stage from the lane index.
+  // The smaller tiles keep every load's offset in a register.  The 256 x 384 tile has
+  // no room for ten (its accumulators take 192 of the wave's 256 registers) and keeps
+  // two: with g = wave * L + u, bit 2 of the swizzle is g's parity, so the offset is
+  // 16 g K (uniform) + lb0 or lb0 ^ 64 (per lane; K a multiple of 64 leaves bits 4..6
+  // of the row term clear), one vector add per load.  Recomputing each offset from the
+  // lane index took ~8 vector instructions per load (2048 x 12288 x 12288: 1332 ->
+  // 1360 TFLOP/s in alternating runs, bitwise the same).
   constexpr bool kKeepOffsets = BN < 384;
   uint32_t xo[C::XL], wo[C::WL];
   auto offset = [&](int row, int ln) __attribute__((always_inline)) {
@@ -180,19 +185,27 @@ __device__ __forceinline__ void gemm_lds_body(const GemmArgs& p, int nb1, int nm
 #pragma unroll
     for (int u = 0; u < C::WL; ++u) wo[u] = offset(8 * (wave * C::WL + u) + (lane >> 3), lane);
   }
+  const uint32_t lb0 = (uint32_t)((lane >> 3) * K * 2 + (((lane & 7) ^ ((lane >> 4) & 3)) << 4));
+  const uint32_t lb1 = lb0 ^ 64u;
+  // offset of load u (group g) without a kept offset; the parity is u's when both
+  // per-wave load counts are even.  opaque() keeps the compiler from hoisting all
+  // ten sums out of the loop into registers the tile does not have.
+  auto group_off = [&](int g, int u) __attribute__((always_inline)) {
+    const bool odd = (C::XL % 2 == 0 && C::WL % 2 == 0) ? (u & 1) : (g & 1);
+    return (uint32_t)opaque((int)(odd ? lb1 : lb0)) + (uint32_t)(g * 16 * K);
+  };
   const int kst0 = SPLIT ? split * p.kps : 0;  // first k stage of this range
   // load u of stage kt into buffer b (u < XL: rows of X, else rows of W)
   auto load_one = [&](int kt, auto b, int u) __attribute__((always_inline)) {
     const int koff = (kst0 + kt) * BK * 2;
-    const int ln = kKeepOffsets ? lane : opaque(lane);
     if (u < C::XL)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xr, (lds_void_t*)(xbuf(b) + (wave * C::XL + u) * 512), 16,
-          kKeepOffsets ? xo[u] : offset(8 * (wave * C::XL + u) + (ln >> 3), ln), koff, 0, 0);
+          kKeepOffsets ? xo[u] : group_off(wave * C::XL + u, u), koff, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wr, (lds_void_t*)(wbuf(b) + (wave * C::WL + (u - C::XL)) * 512), 16,
-          kKeepOffsets ? wo[u - C::XL] : offset(8 * (wave * C::WL + (u - C::XL)) + (ln >> 3), ln),
+          kKeepOffsets ? wo[u - C::XL] : group_off(wave * C::WL + (u - C::XL), u - C::XL),
           koff, 0, 0);
   };
   auto load_stage = [&](int kt, auto b) __attribute__((always_inline)) {
