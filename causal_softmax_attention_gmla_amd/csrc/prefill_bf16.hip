@@ -76,6 +76,7 @@ __shared__ __align__(16) bf16 lds_k0[TILE];
 __shared__ __align__(16) bf16 lds_k1[TILE];
 __shared__ __align__(16) bf16 lds_v0[TILE];
 __shared__ __align__(16) bf16 lds_v1[TILE];
+__shared__ __align__(16) bf16 lds_q[TILE];  // Q rows of waves 0 and 1 while a block starts
 template <int B> __device__ __forceinline__ bf16* k_buf() { return B ? lds_k1 : lds_k0; }
 template <int B> __device__ __forceinline__ bf16* v_buf() { return B ? lds_v1 : lds_v0; }
 
@@ -128,7 +129,7 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, bf16* dst, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, off, 0, 0, 0);
 }
 
-template <bool VARLEN>
+template <bool VARLEN, bool QLDS = true>
 __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b, const int h,
                                               const int qb);
 
@@ -163,8 +164,10 @@ __device__ __forceinline__ void prefill_body(const PrefillArgs& a, int nqb, int 
 
 // One query block: queries qb*BM .. qb*BM + BM - 1 of (batch b, head h), all key tiles it
 // may see.  Leaves LDS in use until it returns (the caller separates two blocks with a
-// barrier).
-template <bool VARLEN>
+// barrier).  QLDS: the Q rows pass through LDS (a fifth 16 KB buffer, 80 KB per
+// workgroup); the latent-fused kernel, whose workgroups need a little more LDS, loads
+// them straight into registers.
+template <bool VARLEN, bool QLDS>
 __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b, const int h,
                                               const int qb) {
   const int q0 = qb * BM;
@@ -206,16 +209,37 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
   const int hh = lane >> 5;
   const int64_t st = a.st;
 
-  // ---- this lane's query row and its Q fragments (B operand of S^T = K Q^T)
+  // ---- this lane's query row and its Q fragments (B operand of S^T = K Q^T).  The
+  // wave's 32 Q rows go to LDS as whole 256-byte rows (LDS-direct, like the tiles; waves
+  // 0, 1 into lds_q, waves 2, 3 into V buffer 1, which the first iteration refills) and
+  // come back as fragments after the first barrier.  16-byte register loads of one
+  // query row per lane touch 32 rows per instruction and made a block's start ~2 us
+  // longer (alternating runs, bitwise the same: B4 T1024 +4%, B1 T2048 gated +1%, B2
+  // T4096 +0.3%).  Rows past the end arrive as zeros (the load range ends there).
   const int wq0 = q0 + wave * 32;  // first query of this wave
   const int tq = wq0 + l32;        // this lane's query
   bf16x8 qf[8];
+  char* const q_lds = (char*)(wave < 2 ? lds_q : lds_v1) + (wave & 1) * 8192;
+  const bool qlds = QLDS && 31 * a.qst + HD < ((int64_t)1 << 30);  // 32-bit offsets
+  if (qlds) {
+    const int qrows = min(32, T - wq0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Qh + (int64_t)wq0 * a.qst), (short)0,
+        qrows > 0 ? (int)(((int64_t)(qrows - 1) * a.qst + HD) * 2) : 0, kBufferDword3);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    if (tq < T)
-      qf[ks] = *(const bf16x8*)(Qh + (int64_t)tq * a.qst + ks * 16 + hh * 8);
-    else
-      qf[ks] = bf16x8{};
+    for (int u = 0; u < 8; ++u) {
+      const int row = 4 * u + (lane >> 4);
+      load_lds16(r, (bf16*)(q_lds + u * 1024),
+                 (uint32_t)((row * a.qst + k_chunk(row, lane & 15) * 8) * 2));
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (tq < T)
+        qf[ks] = *(const bf16x8*)(Qh + (int64_t)tq * a.qst + ks * 16 + hh * 8);
+      else
+        qf[ks] = bf16x8{};
+    }
   }
 
   // ---- key tiles this workgroup visits
@@ -325,6 +349,12 @@ __device__ __forceinline__ void prefill_block(const PrefillArgs& a, const int b,
   load_v(0, B0{});
   load_k(1, B1{});
   tile_barrier();
+  if (qlds) {
+    // row l32, logical chunk 2 ks + hh (the K tiles' swizzle: conflict-free)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      qf[ks] = *(const bf16x8*)(q_lds + l32 * 256 + (k_chunk(l32, 2 * ks + hh) << 4));
+  }
   f32x16 s_cur[2];
   scores(B0{}, s_cur);
   if (0 >= mask_from) mask(s_cur, 0);
@@ -756,7 +786,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_latent_kernel(LatentPrefi
         }
       }
       __syncthreads();
-      prefill_block<false>(f.p, head_lin / f.p.H, head_lin % f.p.H, qb);
+      prefill_block<false, false>(f.p, head_lin / f.p.H, head_lin % f.p.H, qb);
     }
   }
 }

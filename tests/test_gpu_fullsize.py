@@ -88,6 +88,29 @@ def test_prefill_offsets_past_2_31_sampled():
     del qkv, out
 
 
+def test_prefill_query_token_stride_past_lds_load_offsets():
+    """Q rows 2^25 + 2^21 elements apart: 31 rows span more than 2^30 elements, past the 32-bit
+    byte offsets of the LDS-direct Q row loads, so the kernel loads each lane's query
+    row into registers instead (through the chunk entry, whose Q strides are its own);
+    every row against the oracle."""
+    dev = need_gpu()
+    T, D, qst = 40, 128, 2 ** 25 + 2 ** 21
+    assert 31 * qst + D >= 2 ** 30
+    announce(f"prefill T={T}: query token stride {qst} elements")
+    buf = torch.empty((T - 1) * qst + D, dtype=torch.bfloat16, device=dev)
+    q = buf.as_strided((1, T, 1, D), (T * qst, qst, D, 1))
+    q.copy_(I.normal((1, T, 1, D), torch.bfloat16, dev, seed=5300))
+    k = I.normal((1, T, 1, D), torch.bfloat16, dev, seed=5301)
+    v = I.normal((1, T, 1, D), torch.bfloat16, dev, seed=5302)
+    out = torch.full((1, T, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    gm.attend_chunk(q, k, v, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.attend_head(host(q[0, :, 0]), host(k[0, :, 0]), host(v[0, :, 0]),
+                             1 / np.sqrt(D), True)
+    check_rows_rel(host(out[0]), ref, D)
+    del buf, out
+
+
 def test_latent_down_projection_split_k_every_row():
     """The layer's latent down-projection C = X W_c^T (2048 x 512 x 12288) on the split-K
     path: every row against the oracle."""
