@@ -28,7 +28,8 @@
 //    LDS-direct form: no register staging, no vector ALU work).  Each load range ends
 //    at the last valid row, so rows past the sequence end arrive as zeros with no
 //    per-lane predicate.  Both tiles are row-major with the 16-byte chunks of each row
-//    XOR-swizzled so that the fragment reads are free of bank conflicts.
+//    XOR-swizzled so that the fragment reads are free of bank conflicts.  A block's Q
+//    rows take the same path once, at its start, and are read back as fragments.
 //  * The value operand is read with the transposing LDS load ds_read_b64_tr_b16:
 //    each 16-lane group gathers 16 consecutive channels of 4 keys, which is exactly
 //    the A-operand layout of O^T = V^T P^T for the keys the lane's P^T registers hold.
